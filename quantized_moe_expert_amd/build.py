@@ -1,0 +1,72 @@
+"""Build libmoe_iq4nl.so (and the synthetic-input library) for gfx950 with hipcc, in-tree.
+
+Every source is compiled to an object in parallel, then linked.  All HIP code is compiled
+with packed-fp32 instruction selection disabled.
+"""
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-result"]
+
+LIBS = {
+    os.path.join(PKG, "libmoe_iq4nl.so"): [
+        os.path.join(PKG, "csrc", f) for f in
+        ("api.hip", "quant.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip",
+         "combine.hip")],
+    os.path.join(ROOT, "synth", "libmoe_synth.so"): [
+        os.path.join(ROOT, "synth", "csrc", "synth.hip")],
+}
+
+
+def _compile(src, obj, verbose):
+    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (r.stderr or "").splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
+    if verbose and errs.strip():
+        print(errs, flush=True)
+    return obj
+
+
+def build(verbose: bool = False, jobs: int = None) -> list:
+    out_dir = os.path.join(ROOT, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    built = []
+    tasks = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for lib, srcs in LIBS.items():
+            for s in srcs:
+                obj = os.path.join(out_dir, os.path.basename(s) + ".o")
+                tasks.append(ex.submit(_compile, s, obj, verbose))
+        for t in tasks:
+            t.result()
+    for lib, srcs in LIBS.items():
+        objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed for {lib}:\n{r.stderr}")
+        os.replace(tmp, lib)
+        built.append(lib)
+        if verbose:
+            print("built", lib, flush=True)
+    return built
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

@@ -1,0 +1,240 @@
+// C-ABI entry points of libmoe_iq4nl.so: host-side checks, workspace layout, launches on the
+// caller's stream.  Declarations and contracts: include/moe_iq4nl.h.
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/moe_iq4nl.h"
+#include "kernels.h"
+
+namespace moe {
+
+static thread_local int32_t g_last_hip_error = 0;
+
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace moe
+
+using moe::Shape;
+
+namespace {
+
+constexpr size_t kHeaderBytes = 256;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  moe::g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->hidden < 64 || d->hidden > 8192 || d->hidden % 64) return MOE_ERR_SHAPE;
+  if (d->ffn < 64 || d->ffn > 8192 || d->ffn % 64) return MOE_ERR_SHAPE;
+  if (d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_SHAPE;
+  if (d->n_experts < 1 || d->n_experts + d->n_shared > 1024) return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 32) return MOE_ERR_SHAPE;
+  if (d->gating != MOE_GATING_SIGMOID && d->gating != MOE_GATING_SOFTMAX)
+    return MOE_ERR_UNSUPPORTED;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+  if (d->max_tokens < 1) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status check_tokens(const moe_desc* d, int32_t T) {
+  if (T < 0 || T > d->max_tokens) return MOE_ERR_SHAPE;
+  // every slot index and row offset must fit int32 arithmetic on the device
+  if ((int64_t)T * (d->top_k + d->n_shared) > (int64_t)1 << 30) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+Shape shape_of(const moe_desc* d) {
+  return Shape{d->hidden, d->ffn, d->n_experts, d->top_k, d->n_shared, d->gating,
+               d->renormalize};
+}
+
+size_t logits_bytes(const moe_desc* d, int32_t T) { return align256((size_t)T * d->n_experts * 4); }
+
+size_t ws_bytes_for(const moe_desc* d, int32_t T) {
+  return kHeaderBytes + logits_bytes(d, T) + align256(moe::permute_scratch_bytes(shape_of(d), T));
+}
+
+moe_status check_bank(const moe_desc* d, const moe_bank* bank) {
+  if (!bank || !bank->base) return MOE_ERR_NULL;
+  const int64_t esz = 2 * (int64_t)d->ffn * (d->hidden / 32) * 18 +
+                      (int64_t)d->hidden * (d->ffn / 32) * 18;
+  if (bank->expert_stride < esz) return MOE_ERR_SHAPE;
+  if (!aligned(bank->base, 16) || bank->expert_stride % 16) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a supported multiple";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size() reported";
+    case MOE_ERR_UNSUPPORTED: return "unsupported enum value or feature";
+    case MOE_ERR_HIP: return "a HIP launch failed (see moe_last_hip_error)";
+    case MOE_ERR_ALIGNMENT: return "a pointer or stride violates the alignment contract";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_last_hip_error(void) { return moe::g_last_hip_error; }
+
+moe_status moe_workspace_size(const moe_desc* desc, int32_t n_tokens, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_ERR_SHAPE;
+  *bytes = ws_bytes_for(desc, n_tokens);
+  return MOE_OK;
+}
+
+moe_status moe_quantize_iq4nl(const float* w, int64_t n_blocks, uint8_t* out,
+                              hipStream_t stream) {
+  if (n_blocks < 0) return MOE_ERR_SHAPE;
+  if (n_blocks == 0) return MOE_OK;
+  if (!w || !out) return MOE_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(out, 2)) return MOE_ERR_ALIGNMENT;
+  if (n_blocks > ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_quantize(w, n_blocks, out, stream));
+}
+
+moe_status moe_dequantize_iq4nl(const uint8_t* blocks, int64_t n_blocks, float* out,
+                                hipStream_t stream) {
+  if (n_blocks < 0) return MOE_ERR_SHAPE;
+  if (n_blocks == 0) return MOE_OK;
+  if (!blocks || !out) return MOE_ERR_NULL;
+  if (!aligned(blocks, 2) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
+  if (n_blocks > ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_dequantize(blocks, n_blocks, out, stream));
+}
+
+moe_status moe_route(const moe_desc* desc, const float* x, const float* w_router,
+                     const float* bias, int32_t n_tokens, int32_t* topk_ids, float* topk_w,
+                     float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_ERR_ALIGNMENT;
+  if (!logits) {
+    if (!ws) return MOE_ERR_NULL;
+    if (ws_bytes < kHeaderBytes + logits_bytes(desc, n_tokens)) return MOE_ERR_WORKSPACE;
+    logits = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kHeaderBytes);
+  }
+  return hip_status(moe::launch_route(shape_of(desc), x, w_router, bias, n_tokens, topk_ids,
+                                      topk_w, logits, stream));
+}
+
+moe_status moe_permute(const moe_desc* desc, int32_t* topk_ids, float* topk_w,
+                       int32_t n_tokens, const float* x, void* x_perm, int32_t x_perm_dtype,
+                       int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (!offsets || !ws) return MOE_ERR_NULL;
+  if (n_tokens > 0 && (!topk_ids || !topk_w || !sorted_pairs || !pair_slot)) return MOE_ERR_NULL;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_NULL;
+  if (x_perm && x_perm_dtype != MOE_DTYPE_F32 && x_perm_dtype != MOE_DTYPE_BF16)
+    return MOE_ERR_UNSUPPORTED;
+  if (x && (!aligned(x, 16) || !aligned(x_perm, 16))) return MOE_ERR_ALIGNMENT;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < ws_bytes_for(desc, n_tokens)) return MOE_ERR_WORKSPACE;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  int32_t* invalid = reinterpret_cast<int32_t*>(w8);
+  void* scratch = w8 + kHeaderBytes + logits_bytes(desc, n_tokens);
+  return hip_status(moe::launch_permute(shape_of(desc), topk_ids, topk_w, n_tokens, x, x_perm,
+                                        x_perm_dtype == MOE_DTYPE_BF16, offsets, sorted_pairs,
+                                        pair_slot, invalid, scratch, stream));
+}
+
+moe_status moe_expert_gemv_iq4nl(const moe_desc* desc, int32_t stage, const moe_bank* bank,
+                                 const int32_t* offsets, const int32_t* sorted_pairs,
+                                 const float* in, float* out, int32_t n_tokens, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_bank(desc, bank)) != MOE_OK) return st;
+  if (n_tokens == 0) return MOE_OK;
+  if (!offsets || !in || !out) return MOE_ERR_NULL;
+  if (stage == MOE_STAGE_GATE_UP && !sorted_pairs) return MOE_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(out, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moe::launch_gemv(shape_of(desc), stage, bank->base, bank->expert_stride,
+                                     offsets, sorted_pairs, in, out, n_tokens, stream));
+}
+
+moe_status moe_grouped_gemm_iq4nl(const moe_desc* desc, int32_t stage, const moe_bank* bank,
+                                  const int32_t* offsets, const void* in_bf16, void* out,
+                                  int32_t n_tokens, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_bank(desc, bank)) != MOE_OK) return st;
+  // tiles: K in steps of 128, DOWN output columns in tiles of 128
+  if (desc->hidden % 128 || desc->ffn % 128) return MOE_ERR_SHAPE;
+  if (n_tokens == 0) return MOE_OK;
+  if (!offsets || !in_bf16 || !out) return MOE_ERR_NULL;
+  if (!aligned(in_bf16, 16) || !aligned(out, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moe::launch_gemm(shape_of(desc), stage, bank->base, bank->expert_stride,
+                                     offsets, in_bf16, out, n_tokens, stream));
+}
+
+moe_status moe_combine(const moe_desc* desc, const float* o, const int32_t* pair_slot,
+                       const float* topk_w, int32_t n_tokens, const float* residual, float* y,
+                       hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (n_tokens == 0) return MOE_OK;
+  if (!o || !pair_slot || !topk_w || !y) return MOE_ERR_NULL;
+  if (!aligned(o, 16) || !aligned(y, 16) || (residual && !aligned(residual, 16)))
+    return MOE_ERR_ALIGNMENT;
+  return hip_status(moe::launch_combine(shape_of(desc), o, pair_slot, topk_w, n_tokens,
+                                        residual, y, stream));
+}
+
+moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* y,
+                       hipStream_t stream) {
+  if (n_tokens < 0 || hidden <= 0 || hidden % 4) return MOE_ERR_SHAPE;
+  if (!(eps >= 0.0f)) return MOE_ERR_SHAPE;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !y) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moe::launch_rmsnorm(x, n_tokens, hidden, eps, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Prefill path: grouped GEMM of each expert's slot range against its IQ4_NL weights on bf16
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// Xolotl ("DeepSeek-V4.1-Flash at 27 Tokens/s on One RTX 4090"), section "Prompts: fast, and
+// exact": a prompt chunk runs each layer's experts as one batched multiply.  Red Lite "What we
+// learned", section "3. Speed by release": batched matrix kernels for the experts.
+//
+// Tiles: 128 slot rows x 128 weight rows per workgroup (4 waves, 2 x 2, 64 x 64 each), K in
+// steps of 4 IQ4_NL blocks.  Weight tiles are dequantised once per workgroup into LDS as
+// bf16(d * c[q]) (fp32 product, exact; one RNE rounding); activation tiles are staged through
+// LDS.  Inside every 32-wide block both operands use the same K order -- pair j holds
+// elements (j, j+16) -- which is the order of the code bytes, so a code byte dequantises to
+// one packed bf16 pair.  For GATE_UP the workgroup's 128 weight rows are 64 gate rows and the
+// 64 matching up rows, arranged so that a lane holds g and u of the same output and applies
+// SwiGLU in registers.
+//
+// The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 128) over the
+// experts); a persistent grid walks it, so nothing depends on host-known expert loads.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kBM = 128;               // slot rows per tile
+constexpr int kBN = 128;               // weight rows per tile
+constexpr int kKB = 4;                 // IQ4_NL blocks per K step (128 k)
+constexpr int kLdsStride = kKB * 16 + 4;   // dwords per LDS row (bf16 pairs + pad)
+constexpr int kGemmThreads = 256;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool GATEUP>
+__global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ in, void* __restrict__ out, int H, int F, int E, int S) {
+  __shared__ __attribute__((aligned(16))) uint32_t sA[kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint32_t sB[kBN * kLdsStride];
+  __shared__ float2 s_tab[256];
+  __shared__ int s_pref[1024];
+  __shared__ int s_part[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, c16 = lane & 15;
+
+  s_tab[tid] = make_float2((float)kCodebook[tid & 15], (float)kCodebook[tid >> 4]);
+
+  // ---- tile prefix over experts: s_pref[e] = sum_{e' <= e} ceil(m_e' / kBM) ----
+  const int nbins = E + S;
+  int loc[4];
+  int run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    int t = 0;
+    if (e < nbins) t = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+    run += t;
+    loc[i] = run;
+  }
+  int incl = run;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) s_part[wave] = incl;
+  __syncthreads();
+  int before = incl - run;
+  for (int w = 0; w < wave; ++w) before += s_part[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < 1024) s_pref[e] = before + loc[i];
+  }
+  __syncthreads();
+  const int total_m = s_pref[nbins - 1];
+
+  const int K = GATEUP ? H : F;
+  const int NB = K >> 5;
+  const int NKT = NB / kKB;
+  const int NT = GATEUP ? F / 64 : H / kBN;
+  const int64_t row_bytes = (int64_t)NB * kBlockBytes;
+  const int64_t mat_off = GATEUP ? 0 : 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+
+  for (int tile = blockIdx.x; tile < total_m * NT; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile % NT;
+    // expert owning M-tile mt: first e with s_pref[e] > mt
+    int lo = 0, hi = nbins - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] > mt) hi = mid; else lo = mid + 1;
+    }
+    const int e = lo;
+    const int m0 = (mt - (e ? s_pref[e - 1] : 0)) * kBM;
+    const int slot0 = offsets[e];
+    const int rows_valid = min(kBM, offsets[e + 1] - slot0 - m0);
+    const uint8_t* wmat = bank + (int64_t)e * stride + mat_off;
+
+    // weight rows this thread dequantises (2 units: LDS row n, block kk)
+    const uint8_t* brow[2];
+    int bn[2], bk[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + kGemmThreads * i;
+      const int n = v >> 2;
+      bn[i] = n;
+      bk[i] = v & 3;
+      int wr;
+      if (GATEUP) {
+        const int half = n >> 6, rr = n & 63;
+        wr = (rr < 32) ? (nt * 64 + 32 * half + rr) : (F + nt * 64 + 32 * half + rr - 32);
+      } else {
+        wr = nt * kBN + n;
+      }
+      brow[i] = wmat + (int64_t)wr * row_bytes;
+    }
+    // activation rows this thread stages (4 units: row, block, half)
+    const uint16_t* arow[4];
+    int ar[4], ak[4], ac[4];
+    bool aok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + kGemmThreads * i;
+      ar[i] = u >> 3;
+      ak[i] = (u >> 1) & 3;
+      ac[i] = u & 1;
+      aok[i] = ar[i] < rows_valid;
+      arow[i] = in + (int64_t)(slot0 + m0 + (aok[i] ? ar[i] : 0)) * K;
+    }
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = 0; kt < NKT; ++kt) {
+      // global loads for this K step
+      uint4 ga[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* src = arow[i] + (kt * kKB + ak[i]) * 32 + 8 * ac[i];
+        if (aok[i]) {
+          ga[i][0] = *reinterpret_cast<const uint4*>(src);
+          ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
+        } else {
+          ga[i][0] = make_uint4(0, 0, 0, 0);
+          ga[i][1] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      RawBlock gb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) gb[i] = load_block(brow[i], kt * kKB + bk[i]);
+
+      __syncthreads();   // everyone is done reading the previous tile
+      // A -> LDS in pair order: dword j = (a[j], a[j+16])
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0[4] = {ga[i][0].x, ga[i][0].y, ga[i][0].z, ga[i][0].w};
+        const uint32_t a1[4] = {ga[i][1].x, ga[i][1].y, ga[i][1].z, ga[i][1].w};
+        uint32_t d[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          d[2 * w] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+          d[2 * w + 1] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(&sA[ar[i] * kLdsStride + ak[i] * 16 + 8 * ac[i]]);
+        dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+        dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+      }
+      // B -> LDS: dequantise to bf16(d * c) pairs
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bool odd = (bk[i] & 1) != 0;
+        const float dsc = block_scale(gb[i], odd);
+        uint32_t cw[4];
+        block_codes(gb[i], odd, cw);
+        uint32_t o[16];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            const float2 t = s_tab[(cw[cc] >> (8 * y)) & 0xFFu];
+            o[4 * cc + y] = pack_bf16x2(t.x * dsc, t.y * dsc);
+          }
+        uint4* dst = reinterpret_cast<uint4*>(&sB[bn[i] * kLdsStride + bk[i] * 16]);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+        dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        bf16x8_t af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(
+              &sA[(wm * 64 + 16 * i + c16) * kLdsStride + kb * 16 + 4 * q]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+              &sB[(wn * 64 + 16 * j + c16) * kLdsStride + kb * 16 + 4 * q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+
+    // epilogue: lane holds column c16 of each 16x16 sub-tile, rows 4q .. 4q+3
+    if (GATEUP) {
+      uint16_t* hout = static_cast<uint16_t*>(out);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm * 64 + 16 * i + 4 * q + r;
+          if (m >= rows_valid) continue;
+          const int64_t orow = (int64_t)(slot0 + m0 + m) * F;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = nt * 64 + 32 * wn + 16 * j + c16;
+            const float h = silu(acc[i][j][r]) * acc[i][j + 2][r];
+            hout[orow + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xFFFFu);
+          }
+        }
+    } else {
+      float* oout = static_cast<float*>(out);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm * 64 + 16 * i + 4 * q + r;
+          if (m >= rows_valid) continue;
+          const int64_t orow = (int64_t)(slot0 + m0 + m) * H;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oout[orow + nt * kBN + wn * 64 + 16 * j + c16] = acc[i][j][r];
+        }
+    }
+  }
+}
+
+hipError_t launch_gemm(const Shape& sh, int stage, const uint8_t* bank, int64_t stride,
+                       const int32_t* offsets, const void* in, void* out, int T,
+                       hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int grid = device_cu_count() * 2;
+  if (stage == 0)
+    hipLaunchKernelGGL(gemm_kernel<true>, dim3(grid), dim3(kGemmThreads), 0, s, bank, stride,
+                       offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F, sh.E, sh.S);
+  else
+    hipLaunchKernelGGL(gemm_kernel<false>, dim3(grid), dim3(kGemmThreads), 0, s, bank, stride,
+                       offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F, sh.E, sh.S);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,185 @@
+"""GPU parity of whole layers at the workloads' full sizes, through the same C-ABI calls and
+launch configuration that bench.py times.
+
+The oracle is too slow for every token of a 2,048- or 8,192-token chunk, so those tests check
+sampled tokens (a token's output depends only on that token); small batches are checked in
+full.  The 38-layer decode chain is checked against the oracle on its first two layers and by
+properties (finite, bounded RMS, bit-identical reruns, identical HIP-graph replays) on all.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_moe_expert_amd as M
+from quantized_moe_expert_amd import layer as L
+from oracle import moe as omoe
+from synth import generator as G
+from synth.configs import WORKLOADS, TINY, XING4_DECODE
+
+from .helpers import (REL_L2_GEMV, REL_L2_MFMA, assert_close, desc_of, oracle_bank,
+                      oracle_layer, topk_gap)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gpu_layer(wl, T, prefill, layer=0):
+    bank_t, bank = L.make_bank(wl, layer)
+    wr, bias = L.make_router(wl, layer)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(wl.shape, T, prefill=prefill)
+    run = L.prefill_layer if prefill else L.decode_layer
+    y = run(buf, x, wr, bias, bank).clone()
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), buf, (bank_t, bank, wr, bias, x)
+
+
+def _pick_tokens(wl, x, count, seed):
+    """Tokens away from routing near-ties (gap between k-th and (k+1)-th logit)."""
+    s = wl.shape
+    b = G.zipf_bias(wl, 0) if wl.zipf_s is not None else None
+    l = omoe.router_logits(x, G.router_weight(wl, 0), b)
+    ok = np.where(topk_gap(l, s.top_k) > 1e-3)[0]
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(ok, size=min(count, len(ok)), replace=False))
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_tiny_layer_full(prefill):
+    wl = TINY
+    T = wl.decode_tokens[0]
+    y, buf, _ = _gpu_layer(wl, T, prefill)
+    x = G.activations(wl, T)
+    ref, parts = oracle_layer(wl, 0, x, return_parts=True)
+    assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
+    assert_close(y, ref, REL_L2_MFMA if prefill else REL_L2_GEMV, f"tiny prefill={prefill}")
+
+
+@pytest.mark.parametrize("name,T,n_check", [("xing4_decode", 1, 1), ("xing4_decode", 16, 2),
+                                            ("qwen3next_like", 1, 1), ("qwen3next_like", 2, 2),
+                                            ("dsv41_like", 16, 1)])
+def test_decode_layer_full_size(name, T, n_check):
+    wl = WORKLOADS[name]
+    y, buf, _ = _gpu_layer(wl, T, prefill=False)
+    x = G.activations(wl, T)
+    toks = np.arange(T) if n_check >= T else _pick_tokens(wl, x, n_check, T)
+    ref, parts = oracle_layer(wl, 0, x[toks], return_parts=True)
+    assert np.array_equal(buf.ids.cpu().numpy()[toks], parts["ids"])
+    assert_close(y[toks], ref, REL_L2_GEMV, f"{name} T={T}")
+
+
+@pytest.mark.parametrize("name,T,n_check", [("xing4_prefill", 2048, 2), ("qwen3next_like", 2048, 2),
+                                            ("dsv41_like", 8192, 1), ("xing4_prefill", 1, 1)])
+def test_prefill_layer_full_size(name, T, n_check):
+    wl = WORKLOADS[name]
+    y, buf, keep = _gpu_layer(wl, T, prefill=True)
+    assert np.all(np.isfinite(y))
+    x = G.activations(wl, T)
+    toks = _pick_tokens(wl, x, n_check, T)
+    ref, parts = oracle_layer(wl, 0, x[toks], return_parts=True)
+    assert np.array_equal(buf.ids.cpu().numpy()[toks], parts["ids"])
+    assert_close(y[toks], ref, REL_L2_MFMA, f"{name} T={T}")
+    # every token's route is the selection on the GPU's own logits
+    lg = buf.logits.cpu().numpy().astype(np.float64)
+    assert np.array_equal(buf.ids.cpu().numpy(), omoe.select_topk(lg, wl.shape.top_k))
+    # rerun: bit-identical
+    bank_t, bank, wr, bias, xd = keep
+    y2 = L.prefill_layer(buf, xd, wr, bias, bank).clone()
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy(), y)
+
+
+def test_decode_chain_two_layers_vs_oracle():
+    wl = XING4_DECODE
+    s = wl.shape
+    T = 1
+    layers = []
+    for l in range(2):
+        bank_t, bank = L.make_bank(wl, l)
+        wr, bias = L.make_router(wl, l)
+        layers.append((wr, bias, bank, bank_t))
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(s, T)
+    L.decode_chain_step(buf, x, [(a, b, c) for (a, b, c, _) in layers])
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    # oracle chain: x <- x + MoE_l(rmsnorm(x))
+    xr = G.activations(wl, T).astype(np.float64)
+    desc = desc_of(s)
+    for l in range(2):
+        xn = omoe.rmsnorm(xr)
+        wr = G.router_weight(wl, l)
+        _, ids, _ = omoe.route(xn, wr, None, desc)
+        bank, stride = oracle_bank(wl, l, set(ids.reshape(-1).tolist()) | {s.n_experts})
+        xr = xr + omoe.moe_layer(xn, wr, None, bank, stride, desc)
+    assert_close(got, xr, REL_L2_GEMV, "2-layer chain")
+
+
+def test_decode_chain_38_layers_properties_and_graph_replay():
+    wl = XING4_DECODE
+    s = wl.shape
+    T = 1
+    layers, keep = [], []
+    for l in range(wl.layers):
+        bank_t, bank = L.make_bank(wl, l)
+        wr, bias = L.make_router(wl, l)
+        layers.append((wr, bias, bank))
+        keep.append(bank_t)
+    x0 = L.make_activations(wl, T)
+    buf = L.LayerBuffers(s, T)
+    x = x0.clone()
+    rms = []
+    for lay in layers:
+        L.decode_chain_step(buf, x, [lay])
+        rms.append(float(torch.sqrt(torch.mean(x * x)).item()))
+    assert all(np.isfinite(rms)) and max(rms) < 10.0 and min(rms) > 0.5, rms
+    eager = x.clone()
+    # rerun: bit-identical
+    x.copy_(x0)
+    L.decode_chain_step(buf, x, layers)
+    torch.cuda.synchronize()
+    assert torch.equal(x, eager)
+    # HIP graph of the whole 38-layer step; several replays with eager work in between
+    xg = x0.clone()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        L.decode_chain_step(buf, xg, layers)          # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s_)
+    xg.copy_(x0)
+    with torch.cuda.graph(g):
+        L.decode_chain_step(buf, xg, layers)
+    for _ in range(3):
+        xg.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xg, eager)
+        junk = torch.randn(1000, device=DEV).sum()    # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
+
+
+def test_invalid_routes_contribute_nothing():
+    wl = TINY
+    s = wl.shape
+    T = 4
+    bank_t, bank = L.make_bank(wl, 0)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(s, T)
+    ids = np.array([[1, -1], [9, 2], [3, 3], [2 ** 31 - 1, 0]], np.int32)
+    w = np.array([[0.6, 0.4], [0.5, 0.5], [0.2, 0.8], [0.3, 0.7]], np.float32)
+    buf.ids.copy_(torch.from_numpy(ids))
+    buf.w.copy_(torch.from_numpy(w))
+    M.moe_permute(buf.desc, buf.ids, buf.w, T, None, None, 0, buf.offsets, buf.sorted_pairs,
+                  buf.pair_slot, buf.ws, buf.ws_bytes)
+    M.moe_expert_gemv_iq4nl(buf.desc, M.MOE_STAGE_GATE_UP, bank, buf.offsets, buf.sorted_pairs,
+                            x, buf.h, T)
+    M.moe_expert_gemv_iq4nl(buf.desc, M.MOE_STAGE_DOWN, bank, buf.offsets, None, buf.h, buf.o, T)
+    M.moe_combine(buf.desc, buf.o, buf.pair_slot, buf.w, T, None, buf.y)
+    torch.cuda.synchronize()
+    assert int(buf.ws[:4].view(torch.int32).item()) == 3
+    xh = G.activations(wl, T)
+    bank_np, stride = oracle_bank(wl, 0, range(s.n_experts + 1))
+    ref = omoe.moe_layer(xh, None, None, bank_np, stride, desc_of(s), ids=ids, weights=w)
+    assert_close(buf.y.cpu().numpy(), ref, REL_L2_GEMV, "invalid routes")
