@@ -99,9 +99,9 @@ const char *moe_status_string(int32_t status);
 /* HIP error code of the most recent MOE_ERR_HIP on the calling thread (0 if none). */
 int32_t moe_last_hip_error(void);
 
-/* Bytes of the workspace that moe_route, moe_permute, moe_expert_gemv_iq4nl and
- * moe_grouped_gemm_iq4nl need for n_tokens tokens of this layer shape (one size covers all
- * four calls).  Workspace layout: bytes 0..3 hold, after moe_permute, the number of route
+/* Bytes of the workspace that moe_route, moe_permute, moe_expert_gemv_iq4nl,
+ * moe_grouped_gemm_iq4nl and moe_decode_layer need for n_tokens tokens of this layer shape (one size covers all
+ * calls).  Workspace layout: bytes 0..3 hold, after moe_permute, the number of route
  * pairs it sanitised (an int32 the caller may read back); the rest is scratch. */
 moe_status moe_workspace_size(const moe_desc *desc, int32_t n_tokens, size_t *bytes);
 
@@ -184,6 +184,29 @@ moe_status moe_grouped_gemm_iq4nl(const moe_desc *desc, int32_t stage, const moe
 moe_status moe_combine(const moe_desc *desc, const float *o, const int32_t *pair_slot,
                        const float *topk_w, int32_t n_tokens, const float *residual,
                        float *y, hipStream_t stream);
+
+/* Fused decode layer for small batches (1 <= T <= 16): three launches, no host round trip
+ * (PocketLLM page, "Known limitations": decode bound by launch count; Red Lite "1. The idea":
+ * a whole token routed on the GPU).  Computes
+ *   xn = norm_eps >= 0 ? x / sqrt(mean(x^2) + norm_eps) : x        (per row)
+ *   y  = MoE(xn) (+ residual if residual != NULL)
+ * with the routing of moe_route (bias nullable), the permutation of moe_permute, the expert
+ * GEMV arithmetic of moe_expert_gemv_iq4nl and the fixed-order combine of moe_combine.
+ *   x [T, H], residual [T, H], y [T, H] fp32; y may alias x and residual.
+ *   topk_ids [T, k], topk_w [T, k]: optional outputs of the route table (NULL: kept in ws).
+ * stages: bitmask of the launches to enqueue -- MOE_DECODE_ROUTER (logits), MOE_DECODE_GATE_UP
+ * (routing + gate/up), MOE_DECODE_DOWN (down + combine); MOE_DECODE_ALL for the layer.  Split
+ * calls must be enqueued in that order on one stream with the same arguments and workspace.
+ * ws: at least moe_workspace_size(desc, T) bytes, 256-byte aligned; holds the logits, the
+ * permutation and h.  The route table never leaves the device between the launches. */
+#define MOE_DECODE_ROUTER 1
+#define MOE_DECODE_GATE_UP 2
+#define MOE_DECODE_DOWN 4
+#define MOE_DECODE_ALL 7
+moe_status moe_decode_layer(const moe_desc *desc, const moe_bank *bank, const float *w_router,
+                            const float *bias, const float *x, int32_t n_tokens, float norm_eps,
+                            const float *residual, float *y, int32_t *topk_ids, float *topk_w,
+                            int32_t stages, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Weight-free RMSNorm y = x / sqrt(mean(x^2) + eps) over rows of [T, H] fp32: the glue a
  * chain of layers puts between x and each layer's input (y may alias x). */

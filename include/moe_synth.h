@@ -20,12 +20,12 @@ extern "C" {
 
 /* out [n] fp32 device buffer (16-byte aligned not required).  Returns 0 on success, a HIP
  * error code otherwise; n <= 0 enqueues nothing. */
-int32_t synth_normal_f32(float *out, int64_t n, int64_t start, uint32_t seed, uint32_t c2,
+int32_t synth_normal_f32(float *out, int64_t n, uint64_t start, uint32_t seed, uint32_t c2,
                          uint32_t c3, float scale, hipStream_t stream);
 
-/* Raw Philox4x32-10 words for counters (start + j, c1=0 carried in the high word of i):
+/* Raw Philox4x32-10 words for the counters i = start + j (low word, high word, c2, c3):
  * out[4j .. 4j+3] = philox(ctr = (i lo, i hi, c2, c3), key = (seed, key1)).  For checks. */
-int32_t synth_philox_words(uint32_t *out, int64_t n, int64_t start, uint32_t seed,
+int32_t synth_philox_words(uint32_t *out, int64_t n, uint64_t start, uint32_t seed,
                            uint32_t key1, uint32_t c2, uint32_t c3, hipStream_t stream);
 
 #ifdef __cplusplus

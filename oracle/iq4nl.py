@@ -5,7 +5,7 @@ IQ4_NL is 4.5 bits a weight, GGML type 20, 32 weights in 18 bytes.  A block is o
 scale ``d`` plus 32 four-bit indices into a fixed 16-entry signed int8 non-linear codebook;
 a weight is ``d * c[q]``.
 
-Readings where the page is silent (each one listed in the design doc):
+Readings where the page is silent:
 
 * Byte layout: ``d`` little-endian in bytes 0-1; byte ``2+j`` (j < 16) holds index ``q_j``
   in its low nibble and ``q_{j+16}`` in its high nibble.

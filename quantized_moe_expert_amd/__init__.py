@@ -28,6 +28,10 @@ MOE_STAGE_GATE_UP = 0
 MOE_STAGE_DOWN = 1
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_DECODE_ROUTER = 1
+MOE_DECODE_GATE_UP = 2
+MOE_DECODE_DOWN = 4
+MOE_DECODE_ALL = 7
 
 ABI_VERSION = 1
 
@@ -72,6 +76,8 @@ _SIGNATURES = {
     "moe_grouped_gemm_iq4nl": (_I32, [_DESC, _I32, _BANK, _P, _P, _P, _I32, _P, _SZ, _P]),
     "moe_combine": (_I32, [_DESC, _P, _P, _P, _I32, _P, _P, _P]),
     "moe_rmsnorm": (_I32, [_P, _I32, _I32, ctypes.c_float, _P, _P]),
+    "moe_decode_layer": (_I32, [_DESC, _BANK, _P, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P,
+                                _I32, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -186,6 +192,16 @@ def moe_combine(desc, o, pair_slot, topk_w, n_tokens, residual, y, stream=None):
     _check("moe_combine", lib().moe_combine(ctypes.byref(desc), _ptr(o), _ptr(pair_slot),
                                             _ptr(topk_w), n_tokens, _ptr(residual), _ptr(y),
                                             _stream(stream)))
+
+
+def moe_decode_layer(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual, y, topk_ids,
+                     topk_w, ws, ws_bytes, stages=None, stream=None):
+    _check("moe_decode_layer",
+           lib().moe_decode_layer(ctypes.byref(desc), ctypes.byref(bank), _ptr(w_router),
+                                  _ptr(bias), _ptr(x), n_tokens, float(norm_eps), _ptr(residual),
+                                  _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                  MOE_DECODE_ALL if stages is None else stages, _ptr(ws),
+                                  ws_bytes, _stream(stream)))
 
 
 def moe_rmsnorm(x, n_tokens, hidden, eps, y, stream=None):

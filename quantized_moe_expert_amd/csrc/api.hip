@@ -70,8 +70,37 @@ Shape shape_of(const moe_desc* d) {
 
 size_t logits_bytes(const moe_desc* d, int32_t T) { return align256((size_t)T * d->n_experts * 4); }
 
+// Fused decode layer: header | logits | rscale | ids | w | offsets | sorted_pairs | pair_slot |
+// h | o (o only when down + combine cannot be fused).
+struct DecodeLayout {
+  size_t logits, rscale, ids, w, offsets, sp, ps, h, o, total;
+};
+
+DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
+  const size_t P = (size_t)T * d->top_k;
+  const size_t rows = P + (size_t)T * d->n_shared;
+  DecodeLayout L;
+  size_t off = kHeaderBytes;
+  L.logits = off; off += align256((size_t)T * d->n_experts * 4);
+  L.rscale = off; off += align256((size_t)T * 4);
+  L.ids = off; off += align256(P * 4);
+  L.w = off; off += align256(P * 4);
+  L.offsets = off; off += align256((size_t)(d->n_experts + d->n_shared + 1) * 4);
+  L.sp = off; off += align256(P * 4);
+  L.ps = off; off += align256(P * 4);
+  L.h = off; off += align256(rows * d->ffn * 4);
+  L.o = off;
+  if (!moe::decode_down_fused_fits(Shape{d->hidden, d->ffn, d->n_experts, d->top_k,
+                                         d->n_shared, d->gating, d->renormalize}, T))
+    off += align256(rows * d->hidden * 4);
+  L.total = off;
+  return L;
+}
+
 size_t ws_bytes_for(const moe_desc* d, int32_t T) {
-  return kHeaderBytes + logits_bytes(d, T) + align256(moe::permute_scratch_bytes(shape_of(d), T));
+  size_t b = kHeaderBytes + logits_bytes(d, T) + align256(moe::permute_scratch_bytes(shape_of(d), T));
+  if (T <= moe::kDecodeMaxTokens) b = std::max(b, decode_layout(d, T).total);
+  return b;
 }
 
 moe_status check_bank(const moe_desc* d, const moe_bank* bank) {
@@ -225,6 +254,40 @@ moe_status moe_combine(const moe_desc* desc, const float* o, const int32_t* pair
     return MOE_ERR_ALIGNMENT;
   return hip_status(moe::launch_combine(shape_of(desc), o, pair_slot, topk_w, n_tokens,
                                         residual, y, stream));
+}
+
+moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const float* w_router,
+                            const float* bias, const float* x, int32_t n_tokens, float norm_eps,
+                            const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+                            int32_t stages, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (stages < 1 || stages > MOE_DECODE_ALL) return MOE_ERR_UNSUPPORTED;
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (n_tokens > moe::kDecodeMaxTokens) return MOE_ERR_SHAPE;
+  if ((st = check_bank(desc, bank)) != MOE_OK) return st;
+  if (n_tokens == 0) return MOE_OK;
+  if (!w_router || !x || !y || !ws) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(y, 16) ||
+      (residual && !aligned(residual, 16)) || !aligned(ws, 256))
+    return MOE_ERR_ALIGNMENT;
+  if (norm_eps != norm_eps) return MOE_ERR_SHAPE;
+  const DecodeLayout L = decode_layout(desc, n_tokens);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  moe::DecodeScratch sc;
+  sc.logits = reinterpret_cast<float*>(b + L.logits);
+  sc.rscale = reinterpret_cast<float*>(b + L.rscale);
+  sc.ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(b + L.ids);
+  sc.w = topk_w ? topk_w : reinterpret_cast<float*>(b + L.w);
+  sc.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  sc.sorted_pairs = reinterpret_cast<int32_t*>(b + L.sp);
+  sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
+  sc.h = reinterpret_cast<float*>(b + L.h);
+  sc.o = reinterpret_cast<float*>(b + L.o);
+  return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
+                                             w_router, bias, x, n_tokens, norm_eps, residual, y,
+                                             sc, stages, stream));
 }
 
 moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* y,

@@ -95,4 +95,55 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+// DPP lane moves (data-parallel primitives: no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                            0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // row_mirror: lane i <-> 15 - i within 16
+
+// Sum over groups of W consecutive lanes (W a power of two, 2..64), fixed order.  Within a
+// row of 16 lanes a DPP butterfly; across rows, s_readlane of the row sums.  The result is
+// valid in every lane of the group.
+template <int W>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  v += dpp_f<kDppXor1>(v);
+  if constexpr (W >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (W >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (W >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (W == 32) {
+    const int lane = threadIdx.x & 63;
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    v = lane < 32 ? a + b : c + d;
+  } else if constexpr (W == 64) {
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    v = (a + b) + (c + d);
+  }
+  return v;
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads stay in flight across it
+// (__syncthreads() also waits for every outstanding global access of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int group_sum_int(int v, int width) {
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
 }  // namespace moe

@@ -1,0 +1,570 @@
+// Fused decode layer: y = MoE(xn) + residual with xn = x / rms(x) (or xn = x), for small
+// batches (T <= 16), in three kernels a layer.
+//
+// PocketLLM "Xing4.0-29B-A4B", section "Known limitations": a decode step made of thousands of
+// small launches is bound by host submission, and fewer, larger kernels plus graphs are the
+// lever; Red Lite "What we learned", section "1. The idea": a whole token routed on the GPU,
+// with no CPU round trip between layers.  Here every step of the layer stays on the device:
+//
+//   router  : one workgroup per EPW experts; logits of all T tokens from one pass over W_r,
+//             together with sum(x^2) per token (the RMSNorm scale is applied to the dot
+//             product: (W_r x) / rms(x) = W_r (x / rms(x))).
+//   gate/up : every workgroup redoes the top-k and the route histogram of the T tokens
+//             (a few microseconds of LDS work, no cross-workgroup state), picks its expert
+//             (the blockIdx.y-th active one), streams its rows and writes h in slot order;
+//             workgroup (0, 0) also writes the route table and the permutation.
+//   down    : one workgroup per tile of output rows loops over every active expert, keeps
+//             o for its rows in LDS and applies the combine (fixed order: routed j = 0..k-1,
+//             then shared, then residual) before writing y -- no o buffer, no combine launch.
+#include "common.h"
+#include "gemv_core.h"
+#include "kernels.h"
+#include "route_core.h"
+
+namespace moe {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecMaxT = 16;
+constexpr int kDecMaxK = 32;
+#ifndef MOE_DECODE_UP_PASSES
+#define MOE_DECODE_UP_PASSES 8
+#endif
+constexpr int kUpPasses = MOE_DECODE_UP_PASSES;   // weight rows a lane group visits (even)
+constexpr int kDownRing = 16;       // passes in flight in the down kernel
+constexpr int kDownStageUnits = 12; // staging units a thread: rows * F/32 * 4 <= 3072
+
+// ---- router --------------------------------------------------------------------------
+
+template <int EPW>
+__global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
+    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    int T, int H, int E, float eps, int use_norm, float* __restrict__ logits,
+    float* __restrict__ rscale) {
+  __shared__ float s_red[4][(EPW + 1) * kDecMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * EPW;
+  float acc[EPW][kDecMaxT], ss[kDecMaxT];
+#pragma unroll
+  for (int t = 0; t < kDecMaxT; ++t) {
+    ss[t] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < EPW; ++q) acc[q][t] = 0.0f;
+  }
+  // every W_r load of this thread first (H <= 8192: at most 8 float4 a row), then the
+  // activations token by token, each token's loads issued together
+  constexpr int KMAX = 8;
+  const int H4 = H >> 2;
+  float4 w[EPW][KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const int h4 = tid + kDecThreads * i;
+#pragma unroll
+    for (int q = 0; q < EPW; ++q)
+      w[q][i] = (h4 < H4 && e0 + q < E)
+                    ? reinterpret_cast<const float4*>(wr + (size_t)(e0 + q) * H)[h4]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int t = 0; t < kDecMaxT; ++t) {
+    if (t < T) {
+      float4 v[KMAX];
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        const int h4 = tid + kDecThreads * i;
+        v[i] = h4 < H4 ? reinterpret_cast<const float4*>(x + (size_t)t * H)[h4]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        float a = ss[t];
+        a = fmaf(v[i].x, v[i].x, a); a = fmaf(v[i].y, v[i].y, a);
+        a = fmaf(v[i].z, v[i].z, a); a = fmaf(v[i].w, v[i].w, a);
+        ss[t] = a;
+#pragma unroll
+        for (int q = 0; q < EPW; ++q) {
+          float c = acc[q][t];
+          c = fmaf(w[q][i].x, v[i].x, c); c = fmaf(w[q][i].y, v[i].y, c);
+          c = fmaf(w[q][i].z, v[i].z, c); c = fmaf(w[q][i].w, v[i].w, c);
+          acc[q][t] = c;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDecMaxT; ++t) {
+    if (t < T) {
+      const float s0 = group_sum_dpp<64>(ss[t]);
+      if (lane == 0) s_red[wave][EPW * kDecMaxT + t] = s0;
+#pragma unroll
+      for (int q = 0; q < EPW; ++q) {
+        const float s1 = group_sum_dpp<64>(acc[q][t]);
+        if (lane == 0) s_red[wave][q * kDecMaxT + t] = s1;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < EPW * kDecMaxT) {
+    const int q = tid / kDecMaxT, t = tid % kDecMaxT;
+    const int e = e0 + q;
+    if (t < T && e < E) {
+      const float dot = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
+      float r = 1.0f;
+      if (use_norm) {
+        const int i = EPW * kDecMaxT + t;
+        const float sq = (s_red[0][i] + s_red[1][i]) + (s_red[2][i] + s_red[3][i]);
+        r = 1.0f / sqrtf(sq / (float)H + eps);
+      }
+      logits[(size_t)t * E + e] = r * dot + (bias ? bias[e] : 0.0f);
+      if (use_norm && blockIdx.x == 0 && q == 0) rscale[t] = r;
+    }
+  }
+}
+
+// ---- gate/up with in-workgroup routing -------------------------------------------------
+
+template <int LPR, int BPL, int MT>
+__global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const float* __restrict__ x,
+    const float* __restrict__ rscale, const float* __restrict__ logits, int T, int H, int F,
+    int E, int S, int k, int gating, int renorm, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, int32_t* __restrict__ offsets_out,
+    int32_t* __restrict__ sp_out, int32_t* __restrict__ ps_out, float* __restrict__ h_out) {
+  constexpr int RPP = 64 / LPR;
+  constexpr int WROWS = kUpPasses * RPP;
+  constexpr int OROWS = WROWS / 2;
+  extern __shared__ uint32_t s_x[];
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_ids[kDecMaxT * kDecMaxK];
+  __shared__ float s_w[kDecMaxT * kDecMaxK];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_tok[kDecMaxT];
+  __shared__ int s_e, s_slot0, s_m;
+  __shared__ int s_wave[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * k, NBIN = E + S;
+  s_tab[tid] = pair_table_entry(tid);
+  for (int i = tid; i < 1024; i += kDecThreads) s_cnt[i] = 0;
+  for (int t = wave; t < T; t += 4)
+    wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
+  __syncthreads();
+  for (int p = tid; p < P; p += kDecThreads) atomicAdd(&s_cnt[s_ids[p]], 1);   // counts only
+  if (tid < S) s_cnt[E + tid] = T;
+  __syncthreads();
+
+  // the blockIdx.y-th expert with routes, and the number of slots before it
+  if (wave == 0) {
+    const int target = blockIdx.y;
+    int seen = 0, run = 0, found = -1, slot0 = 0;
+    for (int base = 0; base < NBIN && found < 0; base += 64) {
+      const int b = base + lane;
+      const int c = b < NBIN ? s_cnt[b] : 0;
+      const uint64_t mask = __ballot(c > 0);
+      const int cnt = __popcll(mask);
+      if (target < seen + cnt) {
+        uint64_t mm = mask;
+        for (int i = 0; i < target - seen; ++i) mm &= mm - 1;
+        const int pos = __ffsll((long long)mm) - 1;
+        slot0 = run + group_sum_int(lane < pos ? c : 0, 64);
+        found = base + pos;
+      } else {
+        seen += cnt;
+        run += group_sum_int(c, 64);
+      }
+    }
+    if (lane == 0) {
+      s_e = found;
+      s_slot0 = slot0;
+      s_m = found >= 0 ? s_cnt[found] : 0;
+    }
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return;
+  const int slot0 = s_slot0, m = s_m;
+
+  // tokens of expert e, in pair order
+  if (wave == 0) {
+    if (e < E) {
+      int seen = 0;
+      for (int base = 0; base < P; base += 64) {
+        const int p = base + lane;
+        const bool hit = p < P && s_ids[p] == e;
+        const uint64_t mask = __ballot(hit);
+        if (hit) s_tok[seen + __popcll(mask & ((1ull << lane) - 1))] = p / k;
+        seen += __popcll(mask);
+      }
+    } else if (lane < T) {
+      s_tok[lane] = lane;
+    }
+  }
+
+  lds_barrier();                                     // s_tok ready
+
+  // activation loads of the first token tile, then the weight stream (loads complete in
+  // issue order, so the activations arrive first)
+  const int NB = H >> 5;
+  Stager<4 * MT> stg;
+  stg.load(NB, LPR * BPL, min(MT, m), MT,
+           [&](int u) -> const float* { return x + (int64_t)s_tok[u] * H; },
+           [&](int u) { return rscale ? rscale[s_tok[u]] : 1.0f; });
+  // weight loads of this wave (rows stay in registers for every token tile)
+  const int64_t row_bytes = (int64_t)NB * kBlockBytes;
+  const uint8_t* mat = bank + (int64_t)e * stride;
+  const int g = lane / LPR, lig = lane % LPR;
+  const bool odd = (lig & 1) != 0;
+  const int orow0 = (blockIdx.x * (kDecThreads / 64) + wave) * OROWS;
+  RawBlock raw[kUpPasses][BPL];
+#pragma unroll
+  for (int p = 0; p < kUpPasses; ++p) {
+    const int i = p * RPP + g;
+    const int r = orow0 + (i < OROWS ? i : i - OROWS);
+    const bool ok = r < F;
+    const uint8_t* rowp = mat + (int64_t)(ok ? (i < OROWS ? 0 : F) + r : 0) * row_bytes;
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const int kb = lig + LPR * b;
+      raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
+    }
+  }
+
+  // workgroup (0, 0) publishes the route table and the permutation
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    int loc[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      run += b < NBIN ? s_cnt[b] : 0;
+      loc[i] = run;
+    }
+    int incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    lds_barrier();
+    int before = incl - run;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      const int excl = before + (i ? loc[i - 1] : 0);
+      if (b < NBIN) { s_off[b] = excl; offsets_out[b] = excl; }
+      if (b == NBIN - 1) offsets_out[NBIN] = before + loc[i];
+    }
+    lds_barrier();
+    for (int p = tid; p < P; p += kDecThreads) {
+      const int id = s_ids[p];
+      int rank = 0;
+      for (int q = 0; q < p; ++q) rank += (s_ids[q] == id) ? 1 : 0;
+      const int slot = s_off[id] + rank;
+      sp_out[slot] = p;
+      ps_out[p] = slot;
+      ids_out[p] = id;
+      w_out[p] = s_w[p];
+    }
+  }
+
+  for (int t0 = 0; t0 < m; t0 += MT) {
+    const int n_tok = min(MT, m - t0);
+    if (t0) {
+      lds_barrier();
+      stg.load(NB, LPR * BPL, n_tok, MT,
+               [&](int u) -> const float* { return x + (int64_t)s_tok[t0 + u] * H; },
+               [&](int u) { return rscale ? rscale[s_tok[t0 + u]] : 1.0f; });
+    }
+    stg.store(s_x);
+    lds_barrier();
+    float acc[kUpPasses][MT];
+    rows_dot<kUpPasses, LPR, BPL, MT>(raw, odd, s_tab, s_x, lig, acc);
+#pragma unroll
+    for (int p = 0; p < kUpPasses; ++p)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[p][u] = group_sum_dpp<LPR>(acc[p][u]);
+    if (lig == 0) {
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        if (u >= n_tok) continue;
+        const int64_t s = slot0 + t0 + u;
+#pragma unroll
+        for (int p = 0; p < kUpPasses / 2; ++p) {
+          const int r = orow0 + p * RPP + g;
+          if (r < F) h_out[s * F + r] = silu(acc[p][u]) * acc[p + kUpPasses / 2][u];
+        }
+      }
+    }
+  }
+}
+
+// ---- down + combine ------------------------------------------------------------------
+
+// NRP row passes of RPP rows per wave and expert; the workgroup owns 4 * NRP * RPP rows.
+template <int LPR, int BPL, int NRP, int UPT>
+__global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const float* __restrict__ h,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pair_slot,
+    const float* __restrict__ w, int T, int H, int F, int E, int S, int k,
+    const float* residual, float* y) {
+  constexpr int RPP = 64 / LPR;
+  constexpr int RW = NRP * RPP;                  // rows per wave
+  constexpr int R = 4 * RW;                      // rows per workgroup
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_off[1025];
+  __shared__ int s_act[1024];
+  __shared__ int s_nact;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * k, NBIN = E + S;
+  const int rows_total = P + T * S;
+  const int NB = F >> 5;
+  constexpr int NBP = LPR * BPL;                           // block slots a staged row holds
+  uint32_t* s_x = s_dyn;                                   // rows_total x NBP x kXStride
+  float* s_o = reinterpret_cast<float*>(s_dyn + rows_total * NBP * kXStride);  // R x rows
+
+  // every slot's h: loads first (no dependency; they arrive before the weight stream)
+  Stager<UPT> stg;
+  stg.load(NB, NBP, rows_total, rows_total,
+           [&](int u) -> const float* { return h + (int64_t)u * F; }, [&](int) { return 1.0f; });
+  s_tab[tid] = pair_table_entry(tid);
+  for (int i = tid; i <= NBIN; i += kDecThreads) s_off[i] = offsets[i];
+  lds_barrier();
+  // compact list of experts with slots (index order)
+  if (wave == 0) {
+    int seen = 0;
+    for (int base = 0; base < NBIN; base += 64) {
+      const int b = base + lane;
+      const bool ne = b < NBIN && s_off[b + 1] > s_off[b];
+      const uint64_t mask = __ballot(ne);
+      if (ne) s_act[seen + __popcll(mask & ((1ull << lane) - 1))] = b;
+      seen += __popcll(mask);
+    }
+    if (lane == 0) s_nact = seen;
+  }
+  lds_barrier();
+  const int nact = s_nact;
+  const int npass = nact * NRP;
+
+  const int g = lane / LPR, lig = lane % LPR;
+  const bool odd = (lig & 1) != 0;
+  const int r0 = blockIdx.x * R;
+  const int64_t row_bytes = (int64_t)NB * kBlockBytes;
+  const int64_t down_off = 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+
+  auto load_pass = [&](int p, RawBlock (&dst)[BPL]) {
+    const int e = s_act[p / NRP];
+    const int r = r0 + wave * RW + (p % NRP) * RPP + g;
+    const bool ok = r < H;
+    const uint8_t* rowp = bank + (int64_t)e * stride + down_off + (int64_t)(ok ? r : 0) * row_bytes;
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const int kb = lig + LPR * b;
+      dst[b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
+    }
+  };
+
+  RawBlock ring[kDownRing][BPL];
+#pragma unroll
+  for (int d = 0; d < kDownRing; ++d)
+    if (d < npass) load_pass(d, ring[d]);
+
+  // every slot's h -> LDS as bf16 (hi, lo) pairs
+  stg.store(s_x);
+  lds_barrier();
+
+  for (int p0 = 0; p0 < npass; p0 += kDownRing) {
+#pragma unroll
+    for (int d = 0; d < kDownRing; ++d) {
+      const int p = p0 + d;
+      if (p < npass) {
+        const int e = s_act[p / NRP];
+        const int rl = wave * RW + (p % NRP) * RPP + g;          // row within the tile
+        const int sa = s_off[e], sb = s_off[e + 1];
+        for (int u = sa; u < sb; ++u) {
+          float acc[1] = {0.0f};
+#pragma unroll
+          for (int b = 0; b < BPL; ++b) {
+            XBlock<1> xb;
+            xb.load(s_x + u * NBP * kXStride, NBP, lig + LPR * b);
+            block_dot<1>(ring[d][b], odd, s_tab, xb, acc);
+          }
+          const float v = group_sum_dpp<LPR>(acc[0]);
+          if (lig == 0) s_o[rl * rows_total + u] = v;
+        }
+        if (p + kDownRing < npass) load_pass(p + kDownRing, ring[d]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // combine in fixed order: routed j = 0..k-1, then shared experts, then the residual
+  for (int i = tid; i < T * R; i += kDecThreads) {
+    const int t = i / R, rl = i % R;
+    const int r = r0 + rl;
+    if (r >= H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j)
+      acc = fmaf(w[t * k + j], s_o[rl * rows_total + pair_slot[t * k + j]], acc);
+    for (int sidx = 0; sidx < S; ++sidx) acc += s_o[rl * rows_total + P + sidx * T + t];
+    if (residual) acc += residual[(int64_t)t * H + r];
+    y[(int64_t)t * H + r] = acc;
+  }
+}
+
+// ---- host side -------------------------------------------------------------------------
+
+struct DecGeom {
+  int lpr, bpl;
+};
+
+static DecGeom dec_geom(int NB) {
+  DecGeom best{0, 0};
+  int best_waste = 1 << 30;
+  const int lprs[5] = {64, 32, 16, 8, 4};
+  for (int li = 0; li < 5; ++li) {
+    const int bpl = (NB + lprs[li] - 1) / lprs[li];
+    if (bpl > 4) continue;
+    const int waste = lprs[li] * bpl - NB;
+    if (waste < best_waste) {
+      best_waste = waste;
+      best = DecGeom{lprs[li], bpl};
+    }
+  }
+  return best;
+}
+
+static size_t down_lds_bytes(const Shape& sh, int T, int R, int nbp) {
+  const int rows_total = T * (sh.k + sh.S);
+  return (size_t)rows_total * nbp * kXStride * 4 + (size_t)R * rows_total * 4;
+}
+
+constexpr size_t kDownLdsBudget = 96 * 1024;
+
+bool decode_down_fused_fits(const Shape& sh, int T) {
+  const int rows_total = T * (sh.k + sh.S);
+  const DecGeom g = dec_geom(sh.F / 32);
+  const int nbp = g.lpr * g.bpl;
+  return g.lpr > 0 && down_lds_bytes(sh, T, 64, nbp) <= kDownLdsBudget &&
+         rows_total * nbp * 4 <= kDecThreads * kDownStageUnits;
+}
+
+template <int LPR, int BPL, int MT>
+static void launch_up(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t stride,
+                      const float* x, const float* rs, const float* logits, int T,
+                      const Shape& sh, int32_t* ids, float* w, int32_t* off, int32_t* sp,
+                      int32_t* ps, float* h) {
+  const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
+  hipLaunchKernelGGL((decode_gateup_kernel<LPR, BPL, MT>), grid, dim3(kDecThreads), lds, s, bank,
+                     stride, x, rs, logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating,
+                     sh.renorm, ids, w, off, sp, ps, h);
+}
+
+template <int MT>
+static bool dispatch_up(DecGeom gm, dim3 grid, hipStream_t s, const uint8_t* bank,
+                        int64_t stride, const float* x, const float* rs, const float* logits,
+                        int T, const Shape& sh, int32_t* ids, float* w, int32_t* off,
+                        int32_t* sp, int32_t* ps, float* h) {
+#define UP(L, B) \
+  if (gm.lpr == L && gm.bpl == B) { launch_up<L, B, MT>(grid, s, bank, stride, x, rs, logits, T, sh, ids, w, off, sp, ps, h); return true; }
+  UP(64, 1) UP(64, 2) UP(64, 3) UP(64, 4) UP(32, 1) UP(32, 2) UP(32, 3) UP(32, 4)
+  UP(16, 1) UP(16, 2) UP(16, 3) UP(16, 4) UP(8, 1) UP(8, 2) UP(4, 1) UP(4, 2)
+#undef UP
+  return false;
+}
+
+template <int LPR, int BPL, int NRP>
+static void launch_down(hipStream_t s, const uint8_t* bank, int64_t stride, const float* h,
+                        const int32_t* off, const int32_t* ps, const float* w, int T,
+                        const Shape& sh, const float* residual, float* y) {
+  constexpr int R = 4 * NRP * (64 / LPR);
+  const size_t lds = down_lds_bytes(sh, T, R, LPR * BPL);
+  const dim3 grid((sh.H + R - 1) / R);
+  const int units = T * (sh.k + sh.S) * LPR * BPL * 4;
+  if (units <= kDecThreads * 4)
+    hipLaunchKernelGGL((decode_down_combine_kernel<LPR, BPL, NRP, 4>), grid, dim3(kDecThreads),
+                       lds, s, bank, stride, h, off, ps, w, T, sh.H, sh.F, sh.E, sh.S, sh.k,
+                       residual, y);
+  else
+    hipLaunchKernelGGL((decode_down_combine_kernel<LPR, BPL, NRP, kDownStageUnits>), grid,
+                       dim3(kDecThreads), lds, s, bank, stride, h, off, ps, w, T, sh.H, sh.F,
+                       sh.E, sh.S, sh.k, residual, y);
+}
+
+static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_t stride,
+                          const float* h, const int32_t* off, const int32_t* ps, const float* w,
+                          int T, const Shape& sh, const float* residual, float* y) {
+  // rows per workgroup 4 * NRP * RPP: about 16 for every group width
+#define DN(L, B, N) \
+  if (gm.lpr == L && gm.bpl == B) { launch_down<L, B, N>(s, bank, stride, h, off, ps, w, T, sh, residual, y); return true; }
+  DN(64, 1, 4) DN(64, 2, 4) DN(64, 3, 4) DN(64, 4, 4) DN(32, 1, 2) DN(32, 2, 2) DN(32, 3, 2)
+  DN(32, 4, 2) DN(16, 1, 1) DN(16, 2, 1) DN(16, 3, 1) DN(16, 4, 1) DN(8, 1, 1) DN(8, 2, 1)
+  DN(4, 1, 1) DN(4, 2, 1)
+#undef DN
+  return false;
+}
+
+hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
+                              const float* bias, int T, float eps, float* logits,
+                              float* rscale, hipStream_t s) {
+  const int epw = sh.E >= 256 ? 4 : (sh.E >= 128 ? 2 : 1);
+  const int use_norm = eps >= 0.0f ? 1 : 0;
+  const float e_arg = use_norm ? eps : 0.0f;
+  if (epw == 4)
+    hipLaunchKernelGGL(decode_router_kernel<4>, dim3((sh.E + 3) / 4), dim3(kDecThreads), 0, s, x,
+                       wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+  else if (epw == 2)
+    hipLaunchKernelGGL(decode_router_kernel<2>, dim3((sh.E + 1) / 2), dim3(kDecThreads), 0, s, x,
+                       wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+  else
+    hipLaunchKernelGGL(decode_router_kernel<1>, dim3(sh.E), dim3(kDecThreads), 0, s, x, wr, bias,
+                       T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t stride,
+                               const float* wr, const float* bias, const float* x, int T,
+                               float eps, const float* residual, float* y, DecodeScratch sc,
+                               int stages, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int use_norm = eps >= 0.0f ? 1 : 0;
+  hipError_t err = hipSuccess;
+  if (stages & 1) {
+    err = launch_router_rows(sh, x, wr, bias, T, eps, sc.logits, sc.rscale, s);
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 2) {
+
+  // gate/up with routing
+  const DecGeom gu = dec_geom(sh.H / 32);
+  if (gu.lpr == 0) return hipErrorInvalidValue;
+  const int orows_wg = (kDecThreads / 64) * kUpPasses * (64 / gu.lpr) / 2;
+  const int max_active = (int)std::min<int64_t>(sh.E, (int64_t)T * sh.k) + sh.S;
+  dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active);
+  const float* rs = use_norm ? sc.rscale : nullptr;
+  const bool ok = (T > 1 && gu.bpl <= 2)
+      ? dispatch_up<2>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                       sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h)
+      : dispatch_up<1>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                       sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
+  if (!ok) return hipErrorInvalidValue;
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  }
+  if (!(stages & 4)) return hipSuccess;
+
+  // down + combine (fused when every slot's h fits in LDS)
+  if (decode_down_fused_fits(sh, T)) {
+    const DecGeom dn = dec_geom(sh.F / 32);
+    if (!dispatch_down(dn, s, bank, stride, sc.h, sc.offsets, sc.pair_slot, sc.w, T, sh,
+                       residual, y))
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  err = launch_gemv(sh, 1, bank, stride, sc.offsets, nullptr, sc.h, sc.o, T, s);
+  if (err != hipSuccess) return err;
+  return launch_combine(sh, sc.o, sc.pair_slot, sc.w, T, residual, y, s);
+}
+
+}  // namespace moe

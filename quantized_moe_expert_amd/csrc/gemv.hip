@@ -21,12 +21,16 @@
 // for the lo bf16 part of x.  The block sum is scaled by its fp16 d in fp32 and accumulated
 // in fp32.  Row sums are reduced across the LPR lanes by a fixed butterfly.
 #include "common.h"
+#include "gemv_core.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int kGemvThreads = 256;
-constexpr int kPasses = 8;
+#ifndef MOE_GEMV_PASSES
+#define MOE_GEMV_PASSES 8
+#endif
+constexpr int kPasses = MOE_GEMV_PASSES;   // weight rows a lane group visits (even)
 
 // e_slot-th expert (0-based, in index order) whose slot range is non-empty; -1 if none.
 __device__ int find_active_expert(const int32_t* __restrict__ offsets, int n_bins, int e_slot) {
@@ -57,8 +61,10 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   constexpr int RPP = 64 / LPR;               // rows per pass per wave
   constexpr int WROWS = kPasses * RPP;        // weight rows per wave
   constexpr int OROWS = GATEUP ? WROWS / 2 : WROWS;
+  extern __shared__ uint32_t s_x[];           // MT tokens x LPR*BPL blocks x kXStride dwords
   __shared__ uint32_t s_tab[256];
   __shared__ int s_expert;
+  __shared__ int s_row[MT];                   // row index of each staged token in `in`
 
   const int tid = threadIdx.x;
   s_tab[tid] = pair_table_entry(tid);
@@ -87,9 +93,22 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   const bool odd = (lig & 1) != 0;                   // block parity == lane parity
   const int orow0 = (blockIdx.x * (kGemvThreads / 64) + wave) * OROWS;
 
-  // weight rows visited in each pass, and whether they exist
-  const uint8_t* rowp[kPasses];
-  bool rowok[kPasses];
+  // token rows of the first tile (needs sorted_pairs: one dependent L2 round trip)
+  if (tid < MT && tid < m) {
+    const int sl = slot0 + tid;
+    s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+  }
+  lds_barrier();
+
+  // 1) activation loads of the first tile, then every weight load of this wave (loads
+  //    complete in issue order: the activations arrive first); the weight rows stay in
+  //    registers for all token tiles
+  Stager<4 * MT> stg;
+  // (addresses formed from the kernel argument keep the global address space: global loads,
+  //  counted on vmcnt only)
+  stg.load(NB, LPR * BPL, min(MT, m), MT, [&](int u) { return in + (int64_t)s_row[u] * K; },
+           [&](int) { return 1.0f; });
+  RawBlock raw[kPasses][BPL];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int i = p * RPP + g;
@@ -101,111 +120,63 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
       r = orow0 + i;
       wr = r;
     }
-    rowok[p] = r < NOUT;
-    rowp[p] = mat + (int64_t)(rowok[p] ? wr : 0) * row_bytes;
+    const bool ok = r < NOUT;
+    const uint8_t* rowp = mat + (int64_t)(ok ? wr : 0) * row_bytes;
+    // unconditional loads (a lane past the row end reads a block of the same parity inside
+    // it; its activations are zero padding): a static load count, no divergent branches
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const int kb = lig + LPR * b;
+      raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
+    }
   }
 
-  for (int t0 = 0; t0 < m; t0 += MT) {
-    // activations of this lane's blocks, split into bf16 hi/lo pairs (x_j, x_{j+16})
-    uint32_t xh[MT][BPL][16], xl[MT][BPL][16];
+  // 2)-3) per token tile: activations -> LDS (once per workgroup), dequantise and dot.  The
+  // first tile is peeled so that its staging waits only on its own (earlier) loads.
+  auto tile = [&](int t0, int n_tok) {
+    // 3) dequantise and dot
+    float acc[kPasses][MT];
+    rows_dot<kPasses, LPR, BPL, MT>(raw, odd, s_tab, s_x, lig, acc);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[p][u] = group_sum_dpp<LPR>(acc[p][u]);
+    if (lig != 0) return;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-      const int s = slot0 + t0 + u;
-      const bool tok_ok = (t0 + u) < m;
-      const float* src;
+      if (u >= n_tok) continue;
+      const int64_t s = slot0 + t0 + u;
       if (GATEUP) {
-        const int tok = !tok_ok ? 0 : (s < P ? sorted_pairs[s] / k : (s - P) % T);
-        src = in + (int64_t)tok * H;
+#pragma unroll
+        for (int p = 0; p < kPasses / 2; ++p) {
+          const int r = orow0 + p * RPP + g;
+          if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + kPasses / 2][u];
+        }
       } else {
-        src = in + (int64_t)(tok_ok ? s : slot0) * F;
-      }
 #pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const int kb = lig + LPR * b;
-        float v[32];
-        if (kb < NB) {
-          const float4* q = reinterpret_cast<const float4*>(src + kb * 32);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float4 f = q[i];
-            v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) v[i] = 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) split_pair(v[j], v[j + 16], xh[u][b][j], xl[u][b][j]);
-      }
-    }
-
-    // fetch every block this lane needs for all passes, then compute
-    RawBlock raw[kPasses][BPL];
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const int kb = lig + LPR * b;
-        if (rowok[p] && kb < NB) raw[p][b] = load_block(rowp[p], kb);
-        else raw[p][b] = RawBlock{{0u, 0u, 0u, 0u, 0u}};
-      }
-
-    float acc[kPasses][MT];
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-#pragma unroll
-      for (int u = 0; u < MT; ++u) acc[p][u] = 0.0f;
-#pragma unroll
-      for (int b = 0; b < BPL; ++b) {
-        const float d = block_scale(raw[p][b], odd);       // 0 for absent blocks
-        uint32_t c[4];
-        block_codes(raw[p][b], odd, c);
-        float bs[MT];
-#pragma unroll
-        for (int u = 0; u < MT; ++u) bs[u] = 0.0f;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const uint32_t ent = s_tab[(c[cc] >> (8 * y)) & 0xFFu];
-            const int j = 4 * cc + y;
-#pragma unroll
-            for (int u = 0; u < MT; ++u) {
-              bs[u] = dot2_bf16(ent, xh[u][b][j], bs[u]);
-              bs[u] = dot2_bf16(ent, xl[u][b][j], bs[u]);
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < MT; ++u) acc[p][u] = fmaf(d, bs[u], acc[p][u]);
-      }
-    }
-
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-#pragma unroll
-      for (int u = 0; u < MT; ++u) acc[p][u] = group_sum(acc[p][u], LPR);
-
-    if (lig == 0) {
-#pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        if (t0 + u >= m) continue;
-        const int64_t s = slot0 + t0 + u;
-        if (GATEUP) {
-#pragma unroll
-          for (int p = 0; p < kPasses / 2; ++p) {
-            const int r = orow0 + p * RPP + g;
-            if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + kPasses / 2][u];
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < kPasses; ++p) {
-            const int r = orow0 + p * RPP + g;
-            if (r < H) out[s * H + r] = acc[p][u];
-          }
+        for (int p = 0; p < kPasses; ++p) {
+          const int r = orow0 + p * RPP + g;
+          if (r < H) out[s * H + r] = acc[p][u];
         }
       }
     }
+  };
+  stg.store(s_x);
+  lds_barrier();
+  tile(0, min(MT, m));
+  for (int t0 = MT; t0 < m; t0 += MT) {
+    const int n_tok = min(MT, m - t0);
+    lds_barrier();
+    if (tid < n_tok) {
+      const int sl = slot0 + t0 + tid;
+      s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+    }
+    lds_barrier();
+    stg.load(NB, LPR * BPL, n_tok, MT, [&](int u) { return in + (int64_t)s_row[u] * K; },
+             [&](int) { return 1.0f; });
+    stg.store(s_x);
+    lds_barrier();
+    tile(t0, n_tok);
   }
 }
 
@@ -238,7 +209,8 @@ template <int LPR, int BPL, int MT, bool GU>
 static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t stride,
                        const int32_t* offsets, const int32_t* sp, const float* in, float* out,
                        const Shape& sh, int T) {
-  hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), 0, s, bank,
+  const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
+  hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,
                      stride, offsets, sp, in, out, sh.H, sh.F, sh.E, sh.S, sh.k, T);
 }
 

@@ -38,6 +38,30 @@ hipError_t launch_combine(const Shape& sh, const float* o, const int32_t* pair_s
 
 hipError_t launch_rmsnorm(const float* x, int T, int H, float eps, float* y, hipStream_t s);
 
+// Intermediates of the fused decode layer (device pointers inside the caller's workspace).
+struct DecodeScratch {
+  float* logits;          // [T, E]
+  float* rscale;          // [T]
+  int32_t* ids;           // [T, k]
+  float* w;               // [T, k]
+  int32_t* offsets;       // [E + S + 1]
+  int32_t* sorted_pairs;  // [T * k]
+  int32_t* pair_slot;     // [T * k]
+  float* h;               // [rows, F]
+  float* o;               // [rows, H] (only when down + combine cannot be fused)
+};
+
+constexpr int kDecodeMaxTokens = 16;
+// logits (and, with eps >= 0, the RMSNorm scale of each row) for T <= 16 rows
+hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
+                              const float* bias, int T, float eps, float* logits,
+                              float* rscale, hipStream_t s);
+bool decode_down_fused_fits(const Shape& sh, int T);
+hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t stride,
+                               const float* wr, const float* bias, const float* x, int T,
+                               float eps, const float* residual, float* y, DecodeScratch sc,
+                               int stages, hipStream_t s);
+
 int device_cu_count();
 
 }  // namespace moe

@@ -8,8 +8,9 @@ generator (``synth.device``) and the library's own encoder.
 import torch
 
 from . import (MOE_DTYPE_BF16, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, make_bank as _make_bank,
-               make_desc, moe_combine, moe_expert_gemv_iq4nl, moe_grouped_gemm_iq4nl,
-               moe_permute, moe_quantize_iq4nl, moe_rmsnorm, moe_route, moe_workspace_size)
+               make_desc, moe_combine, moe_decode_layer, moe_expert_gemv_iq4nl,
+               moe_grouped_gemm_iq4nl, moe_permute, moe_quantize_iq4nl, moe_rmsnorm, moe_route,
+               moe_workspace_size)
 
 
 def desc_of(shape, max_tokens):
@@ -77,11 +78,26 @@ def prefill_layer(buf, x, w_router, bias, bank, residual=None, out=None):
     return y
 
 
-def decode_chain_step(buf, x, layers, eps=1e-6):
-    """x <- x + MoE_l(rmsnorm(x)) for every (w_router, bias, bank) in layers, in place."""
+def decode_layer_fused(buf, x, w_router, bias, bank, norm_eps=-1.0, residual=None, out=None,
+                       stages=None):
+    """y = MoE(xn) (+ residual) through moe_decode_layer (three launches, T <= 16)."""
+    y = buf.y if out is None else out
+    moe_decode_layer(buf.desc, bank, w_router, bias, x, buf.T, norm_eps, residual, y, buf.ids,
+                     buf.w, buf.ws, buf.ws_bytes, stages=stages)
+    return y
+
+
+def decode_chain_step(buf, x, layers, eps=1e-6, fused=True):
+    """x <- x + MoE_l(rmsnorm(x)) for every (w_router, bias, bank) in layers, in place.
+
+    fused: one moe_decode_layer call a layer (the RMSNorm folded into it); otherwise the
+    separate entry points (rmsnorm, route, permute, two GEMVs, combine)."""
     for (w_router, bias, bank) in layers:
-        moe_rmsnorm(x, buf.T, buf.shape.hidden, eps, buf.xn)
-        decode_layer(buf, buf.xn, w_router, bias, bank, residual=x, out=x)
+        if fused:
+            decode_layer_fused(buf, x, w_router, bias, bank, norm_eps=eps, residual=x, out=x)
+        else:
+            moe_rmsnorm(x, buf.T, buf.shape.hidden, eps, buf.xn)
+            decode_layer(buf, buf.xn, w_router, bias, bank, residual=x, out=x)
     return x
 
 

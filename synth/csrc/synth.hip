@@ -30,11 +30,11 @@ __device__ __forceinline__ void philox10(uint32_t c[4], uint32_t k0, uint32_t k1
   }
 }
 
-__global__ void normal_kernel(float* out, int64_t n, int64_t start, uint32_t seed, uint32_t c2,
+__global__ void normal_kernel(float* out, int64_t n, uint64_t start, uint32_t seed, uint32_t c2,
                               uint32_t c3, float scale) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
-  const uint64_t i = (uint64_t)(start + j);
+  const uint64_t i = start + (uint64_t)j;
   uint32_t c[4] = {(uint32_t)i, (uint32_t)(i >> 32), c2, c3};
   philox10(c, seed, kKey1);
   int32_t s = 0;
@@ -43,11 +43,11 @@ __global__ void normal_kernel(float* out, int64_t n, int64_t start, uint32_t see
   out[j] = (float)(s - 262140) * scale;
 }
 
-__global__ void words_kernel(uint32_t* out, int64_t n, int64_t start, uint32_t seed,
+__global__ void words_kernel(uint32_t* out, int64_t n, uint64_t start, uint32_t seed,
                              uint32_t key1, uint32_t c2, uint32_t c3) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
-  const uint64_t i = (uint64_t)(start + j);
+  const uint64_t i = start + (uint64_t)j;
   uint32_t c[4] = {(uint32_t)i, (uint32_t)(i >> 32), c2, c3};
   philox10(c, seed, key1);
 #pragma unroll
@@ -56,10 +56,10 @@ __global__ void words_kernel(uint32_t* out, int64_t n, int64_t start, uint32_t s
 
 }  // namespace
 
-extern "C" int32_t synth_normal_f32(float* out, int64_t n, int64_t start, uint32_t seed,
+extern "C" int32_t synth_normal_f32(float* out, int64_t n, uint64_t start, uint32_t seed,
                                     uint32_t c2, uint32_t c3, float scale, hipStream_t stream) {
   if (n <= 0) return 0;
-  if (!out || start < 0) return (int32_t)hipErrorInvalidValue;
+  if (!out) return (int32_t)hipErrorInvalidValue;
   const int64_t grid = (n + 255) / 256;
   if (grid > 0x7FFFFFFF) return (int32_t)hipErrorInvalidValue;
   hipLaunchKernelGGL(normal_kernel, dim3((unsigned)grid), dim3(256), 0, stream, out, n, start,
@@ -67,11 +67,11 @@ extern "C" int32_t synth_normal_f32(float* out, int64_t n, int64_t start, uint32
   return (int32_t)hipGetLastError();
 }
 
-extern "C" int32_t synth_philox_words(uint32_t* out, int64_t n, int64_t start, uint32_t seed,
+extern "C" int32_t synth_philox_words(uint32_t* out, int64_t n, uint64_t start, uint32_t seed,
                                       uint32_t key1, uint32_t c2, uint32_t c3,
                                       hipStream_t stream) {
   if (n <= 0) return 0;
-  if (!out || start < 0) return (int32_t)hipErrorInvalidValue;
+  if (!out) return (int32_t)hipErrorInvalidValue;
   const int64_t grid = (n + 255) / 256;
   if (grid > 0x7FFFFFFF) return (int32_t)hipErrorInvalidValue;
   hipLaunchKernelGGL(words_kernel, dim3((unsigned)grid), dim3(256), 0, stream, out, n, start,

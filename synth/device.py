@@ -21,11 +21,11 @@ def lib():
                               "`python -m quantized_moe_expert_amd.build`")
         l = ctypes.CDLL(LIB_PATH)
         l.synth_normal_f32.restype = ctypes.c_int32
-        l.synth_normal_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+        l.synth_normal_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                        ctypes.c_float, ctypes.c_void_p]
         l.synth_philox_words.restype = ctypes.c_int32
-        l.synth_philox_words.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+        l.synth_philox_words.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                          ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                          ctypes.c_uint32, ctypes.c_void_p]
         _lib = l

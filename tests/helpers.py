@@ -77,6 +77,54 @@ def oracle_layer(wl, layer, x, return_parts=False, bias=None, w_router=None):
     return omoe.moe_layer(x, wr, b, bank, stride, desc, return_parts=return_parts)
 
 
+U_BF16 = 2.0 ** -9        # unit roundoff of round-to-nearest-even bf16
+SILU_LIPSCHITZ = 1.0999   # max |d silu / dg| (attained near g = 2.4)
+
+
+def _gamma(K):
+    u = 2.0 ** -24
+    return K * u / (1 - K * u)
+
+
+def bf16_dot_bound(a_abs, K):
+    """Bound on |fp32-accumulated sum of bf16(a_i) * bf16(b_i) - sum a_i b_i| given
+    a_abs = sum |a_i b_i|: each operand rounded once (RNE), products exact in fp32."""
+    e = 2 * U_BF16 + U_BF16 ** 2
+    return (e + _gamma(K) * (1 + U_BF16) ** 2) * a_abs
+
+
+def gate_up_bf16_bound(wg, wu, x):
+    """Elementwise bound on |h_gpu - h| for h = silu(W_g x) * (W_u x) computed from bf16 x and
+    bf16 weights with fp32 accumulation, SwiGLU in fp32 and h rounded to bf16 at the end."""
+    x = np.asarray(x, np.float64)
+    K = x.shape[1]
+    g = x @ wg.T
+    u = x @ wu.T
+    dg = bf16_dot_bound(np.abs(x) @ np.abs(wg).T, K)
+    du = bf16_dot_bound(np.abs(x) @ np.abs(wu).T, K)
+    sg = g / (1 + np.exp(-g))
+    pre = SILU_LIPSCHITZ * dg * (np.abs(u) + du) + np.abs(sg) * du
+    h = np.abs(sg * u)
+    return pre + U_BF16 * (h + pre) + 1e-6 * h
+
+
+def down_bf16_bound(wd, h):
+    h = np.asarray(h, np.float64)
+    return bf16_dot_bound(np.abs(h) @ np.abs(wd).T, h.shape[1])
+
+
+def assert_within_bound(got, ref, bound, rel, what=""):
+    """rel-L2 <= rel and |got - ref| <= bound elementwise."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    r = rel_l2(got, ref)
+    assert r <= rel, f"{what}: rel-L2 {r:.3e} > {rel:.1e}"
+    excess = np.abs(got - ref) - bound
+    assert np.all(excess <= 0), f"{what}: {int(np.sum(excess > 0))} elements beyond the bound"
+    return r
+
+
 def topk_gap(logits, k):
     """Per token: gap between the k-th and (k+1)-th largest logit (inf when k == E)."""
     l = np.sort(np.asarray(logits, np.float64), axis=1)[:, ::-1]

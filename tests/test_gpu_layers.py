@@ -89,7 +89,49 @@ def test_prefill_layer_full_size(name, T, n_check):
     assert np.array_equal(y2.cpu().numpy(), y)
 
 
-def test_decode_chain_two_layers_vs_oracle():
+@pytest.mark.parametrize("name,T,n_check", [("tiny", 4, 4), ("xing4_decode", 1, 1),
+                                            ("xing4_decode", 16, 2), ("qwen3next_like", 1, 1),
+                                            ("qwen3next_like", 2, 2), ("dsv41_like", 16, 1)])
+def test_fused_decode_layer_full_size(name, T, n_check):
+    wl = WORKLOADS[name]
+    s = wl.shape
+    bank_t, bank = L.make_bank(wl, 0)
+    wr, bias = L.make_router(wl, 0)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(s, T)
+    y = L.decode_layer_fused(buf, x, wr, bias, bank).clone()
+    ids = buf.ids.clone()
+    # the unfused entry points on the same inputs: same routes, same outputs within tolerance
+    buf2 = L.LayerBuffers(s, T)
+    y2 = L.decode_layer(buf2, x, wr, bias, bank).clone()
+    # split stages: bit-identical to one call
+    y3 = torch.empty_like(y)
+    for st in (M.MOE_DECODE_ROUTER, M.MOE_DECODE_GATE_UP, M.MOE_DECODE_DOWN):
+        L.decode_layer_fused(buf, x, wr, bias, bank, out=y3, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, buf2.ids)
+    assert torch.equal(y3, y)
+    assert_close(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64), REL_L2_GEMV, "fused vs unfused")
+    xh = G.activations(wl, T)
+    toks = np.arange(T) if n_check >= T else _pick_tokens(wl, xh, n_check, T)
+    ref, parts = oracle_layer(wl, 0, xh[toks], return_parts=True)
+    assert np.array_equal(ids.cpu().numpy()[toks], parts["ids"])
+    assert_close(y.cpu().numpy()[toks], ref, REL_L2_GEMV, f"fused {name} T={T}")
+
+
+def test_fused_decode_rejects_large_batches():
+    wl = XING4_DECODE
+    s = wl.shape
+    desc = L.desc_of(s, 17)
+    bank_t, bank = L.make_bank(wl, 0, experts=[0])
+    x = torch.zeros((17, s.hidden), device=DEV)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_decode_layer(desc, bank, x, None, x, 17, -1.0, None, x, None, None, x, 1 << 20)
+    assert ei.value.status == M.MOE_ERR_SHAPE
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_chain_two_layers_vs_oracle(fused):
     wl = XING4_DECODE
     s = wl.shape
     T = 1
@@ -100,7 +142,7 @@ def test_decode_chain_two_layers_vs_oracle():
         layers.append((wr, bias, bank, bank_t))
     x = L.make_activations(wl, T)
     buf = L.LayerBuffers(s, T)
-    L.decode_chain_step(buf, x, [(a, b, c) for (a, b, c, _) in layers])
+    L.decode_chain_step(buf, x, [(a, b, c) for (a, b, c, _) in layers], fused=fused)
     torch.cuda.synchronize()
     got = x.cpu().numpy()
     # oracle chain: x <- x + MoE_l(rmsnorm(x))
