@@ -56,6 +56,12 @@ class moe_bank(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64)]
 
 
+class moe_layer(ctypes.Structure):
+    _fields_ = [("bank", moe_bank), ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+MOE_CHAIN_MAX_LAYERS = 64
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -76,6 +82,8 @@ _SIGNATURES = {
     "moe_grouped_gemm_iq4nl": (_I32, [_DESC, _I32, _BANK, _P, _P, _P, _I32, _P, _SZ, _P]),
     "moe_combine": (_I32, [_DESC, _P, _P, _P, _I32, _P, _P, _P]),
     "moe_rmsnorm": (_I32, [_P, _I32, _I32, ctypes.c_float, _P, _P]),
+    "moe_decode_chain": (_I32, [_DESC, ctypes.POINTER(moe_layer), _I32, _P, _I32, ctypes.c_float,
+                                _P, _P, _P, _SZ, _P]),
     "moe_decode_layer": (_I32, [_DESC, _BANK, _P, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P,
                                 _I32, _P, _SZ, _P]),
 }
@@ -140,6 +148,10 @@ def moe_status_string(status):
     return lib().moe_status_string(status).decode()
 
 
+def moe_last_hip_error():
+    return lib().moe_last_hip_error()
+
+
 def moe_workspace_size(desc, n_tokens):
     n = _SZ(0)
     _check("moe_workspace_size", lib().moe_workspace_size(ctypes.byref(desc), n_tokens,
@@ -201,6 +213,25 @@ def moe_decode_layer(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual
                                   _ptr(bias), _ptr(x), n_tokens, float(norm_eps), _ptr(residual),
                                   _ptr(y), _ptr(topk_ids), _ptr(topk_w),
                                   MOE_DECODE_ALL if stages is None else stages, _ptr(ws),
+                                  ws_bytes, _stream(stream)))
+
+
+def make_layers(layers):
+    """ctypes array of moe_layer from (bank, w_router, bias) triples (bank: moe_bank)."""
+    arr = (moe_layer * max(1, len(layers)))()
+    for i, (bank, wr, bias) in enumerate(layers):
+        arr[i] = moe_layer(bank, _ptr(wr), _ptr(bias))
+    return arr
+
+
+def moe_decode_chain(desc, layers, n_layers, x, n_tokens, norm_eps, topk_ids, topk_w, ws,
+                     ws_bytes, stream=None):
+    """layers: the ctypes array of make_layers (or a list of triples)."""
+    if not isinstance(layers, ctypes.Array):
+        layers = make_layers(layers)
+    _check("moe_decode_chain",
+           lib().moe_decode_chain(ctypes.byref(desc), layers, n_layers, _ptr(x), n_tokens,
+                                  float(norm_eps), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
                                   ws_bytes, _stream(stream)))
 
 

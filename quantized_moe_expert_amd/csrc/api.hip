@@ -30,7 +30,12 @@ using moe::Shape;
 
 namespace {
 
-constexpr size_t kHeaderBytes = 256;
+// Workspace: bytes 0..3 the sanitised-pair count of moe_permute, 4..7 the status word of
+// moe_decode_chain, 256.. the chain's control counters, then scratch.
+constexpr size_t kStatusOffset = 4;
+constexpr size_t kControlOffset = 256;
+constexpr size_t kHeaderBytes = kControlOffset + moe::kChainControlBytes;
+static_assert(kHeaderBytes % 256 == 0, "scratch alignment");
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -97,9 +102,36 @@ DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
   return L;
 }
 
+// Decode chain: header | kChainMaxLayers blocks, one a layer, each
+//   x | logits | rscale | w | pair_slot | slot_tok | act | h
+struct ChainLayout {
+  size_t x, logits, rscale, w, ps, slot_tok, act, h, block, total;
+};
+
+ChainLayout chain_layout(const moe_desc* d, int32_t T) {
+  const size_t P = (size_t)T * d->top_k;
+  const size_t rows = P + (size_t)T * d->n_shared;
+  ChainLayout L;
+  size_t off = 0;
+  L.x = off; off += align256((size_t)T * d->hidden * 4);
+  L.logits = off; off += align256((size_t)T * d->n_experts * 4);
+  L.rscale = off; off += align256((size_t)T * 4);
+  L.w = off; off += align256(P * 4);
+  L.ps = off; off += align256(P * 4);
+  L.slot_tok = off; off += align256(rows * 4);
+  L.act = off; off += align256((1 + 3 * (size_t)d->n_experts) * 4);
+  L.h = off; off += align256(rows * d->ffn * 4);
+  L.block = off;
+  L.total = kHeaderBytes + (size_t)moe::kChainMaxLayers * off;
+  return L;
+}
+
 size_t ws_bytes_for(const moe_desc* d, int32_t T) {
   size_t b = kHeaderBytes + logits_bytes(d, T) + align256(moe::permute_scratch_bytes(shape_of(d), T));
-  if (T <= moe::kDecodeMaxTokens) b = std::max(b, decode_layout(d, T).total);
+  if (T <= moe::kDecodeMaxTokens) {
+    b = std::max(b, decode_layout(d, T).total);
+    b = std::max(b, chain_layout(d, T).total);
+  }
   return b;
 }
 
@@ -288,6 +320,67 @@ moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
                                              w_router, bias, x, n_tokens, norm_eps, residual, y,
                                              sc, stages, stream));
+}
+
+moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32_t n_layers,
+                            float* x, int32_t n_tokens, float norm_eps, int32_t* topk_ids,
+                            float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(desc, n_tokens)) != MOE_OK) return st;
+  if (n_tokens > moe::kDecodeMaxTokens) return MOE_ERR_SHAPE;
+  if (n_layers < 0 || n_layers > MOE_CHAIN_MAX_LAYERS) return MOE_ERR_SHAPE;
+  if (n_layers > 0 && !layers) return MOE_ERR_NULL;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if ((st = check_bank(desc, &layers[l].bank)) != MOE_OK) return st;
+    if (!layers[l].w_router) return MOE_ERR_NULL;
+    if (!aligned(layers[l].w_router, 16)) return MOE_ERR_ALIGNMENT;
+  }
+  if (n_tokens == 0 || n_layers == 0) return MOE_OK;
+  if (!x || !ws) return MOE_ERR_NULL;
+  if ((topk_ids == nullptr) != (topk_w == nullptr)) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (norm_eps != norm_eps) return MOE_ERR_SHAPE;
+  if (ws_bytes < ws_bytes_for(desc, n_tokens)) return MOE_ERR_WORKSPACE;
+  const Shape sh = shape_of(desc);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  const size_t P = (size_t)n_tokens * desc->top_k;
+  if (moe::chain_supported(sh, n_tokens)) {
+    const ChainLayout L = chain_layout(desc, n_tokens);
+    moe::ChainLayer lay[MOE_CHAIN_MAX_LAYERS];
+    for (int32_t l = 0; l < n_layers; ++l)
+      lay[l] = moe::ChainLayer{layers[l].bank.base, layers[l].bank.expert_stride,
+                               layers[l].w_router, layers[l].bias};
+    moe::ChainScratch sc;
+    sc.control = b + kControlOffset;
+    sc.status = reinterpret_cast<uint32_t*>(b + kStatusOffset);
+    sc.layers = b + kHeaderBytes;
+    sc.layer_stride = (int64_t)L.block;
+    sc.off_x = (int32_t)L.x; sc.off_logits = (int32_t)L.logits; sc.off_rscale = (int32_t)L.rscale;
+    sc.off_w = (int32_t)L.w; sc.off_ps = (int32_t)L.ps; sc.off_slot_tok = (int32_t)L.slot_tok;
+    sc.off_act = (int32_t)L.act; sc.off_h = (int32_t)L.h;
+    return hip_status(moe::launch_decode_chain(sh, lay, n_layers, x, n_tokens, norm_eps,
+                                               topk_ids, topk_w, sc, stream));
+  }
+  // shapes without a persistent configuration: three launches a layer
+  const DecodeLayout L = decode_layout(desc, n_tokens);
+  moe::DecodeScratch sc;
+  sc.logits = reinterpret_cast<float*>(b + L.logits);
+  sc.rscale = reinterpret_cast<float*>(b + L.rscale);
+  sc.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  sc.sorted_pairs = reinterpret_cast<int32_t*>(b + L.sp);
+  sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
+  sc.h = reinterpret_cast<float*>(b + L.h);
+  sc.o = reinterpret_cast<float*>(b + L.o);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    sc.ids = topk_ids ? topk_ids + l * P : reinterpret_cast<int32_t*>(b + L.ids);
+    sc.w = topk_w ? topk_w + l * P : reinterpret_cast<float*>(b + L.w);
+    const moe_status s2 = hip_status(moe::launch_decode_layer(
+        sh, layers[l].bank.base, layers[l].bank.expert_stride, layers[l].w_router,
+        layers[l].bias, x, n_tokens, norm_eps, x, x, sc, MOE_DECODE_ALL, stream));
+    if (s2 != MOE_OK) return s2;
+  }
+  return MOE_OK;
 }
 
 moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* y,

@@ -90,6 +90,15 @@ struct XBlock {
   }
 };
 
+// A copy of a raw block that the compiler must treat as new on every use: the lookups of a
+// block are then formed where it is multiplied instead of being hoisted out of the token
+// loops (which keeps 16 table addresses a block live for the whole kernel).
+__device__ __forceinline__ RawBlock fresh(const RawBlock& r) {
+  RawBlock o = r;
+  asm volatile("" : "+v"(o.w[0]), "+v"(o.w[1]), "+v"(o.w[2]), "+v"(o.w[3]), "+v"(o.w[4]));
+  return o;
+}
+
 // acc[u] += d * sum_j (c[q_j] x_j + c[q_{j+16}] x_{j+16}) over one block, for MT tokens.
 template <int MT>
 __device__ __forceinline__ void block_dot(const RawBlock& raw, bool odd, const uint32_t* s_tab,
@@ -117,7 +126,8 @@ __device__ __forceinline__ void block_dot(const RawBlock& raw, bool odd, const u
 }
 
 // acc[p][u] over all PASSES rows and the lane's BPL blocks: block-major, so only one block
-// of activations is live at a time.
+// of activations is live at a time; a scheduling barrier between blocks keeps the compiler
+// from hoisting every block's LDS reads.
 template <int PASSES, int LPR, int BPL, int MT>
 __device__ __forceinline__ void rows_dot(const RawBlock (&raw)[PASSES][BPL], bool odd,
                                          const uint32_t* s_tab, const uint32_t* s_x, int lig,
@@ -131,7 +141,8 @@ __device__ __forceinline__ void rows_dot(const RawBlock (&raw)[PASSES][BPL], boo
     XBlock<MT> x;
     x.load(s_x, LPR * BPL, lig + LPR * b);
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) block_dot<MT>(raw[p][b], odd, s_tab, x, acc[p]);
+    for (int p = 0; p < PASSES; ++p) block_dot<MT>(fresh(raw[p][b]), odd, s_tab, x, acc[p]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -8,7 +8,8 @@ generator (``synth.device``) and the library's own encoder.
 import torch
 
 from . import (MOE_DTYPE_BF16, MOE_STAGE_DOWN, MOE_STAGE_GATE_UP, make_bank as _make_bank,
-               make_desc, moe_combine, moe_decode_layer, moe_expert_gemv_iq4nl,
+               make_desc, make_layers, moe_combine, moe_decode_chain, moe_decode_layer,
+               moe_expert_gemv_iq4nl,
                moe_grouped_gemm_iq4nl, moe_permute, moe_quantize_iq4nl, moe_rmsnorm, moe_route,
                moe_workspace_size)
 
@@ -36,7 +37,8 @@ class LayerBuffers:
         self.sorted_pairs = torch.empty(max(T * s.top_k, 1), **i32)
         self.pair_slot = torch.empty(max(T * s.top_k, 1), **i32)
         self.ws_bytes = moe_workspace_size(self.desc, T)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        # zero-filled: moe_decode_chain's control counters start at zero
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
         if prefill:
             self.x_perm = torch.empty((rows, s.hidden), dtype=torch.bfloat16, device=device)
             self.h = torch.empty((rows, s.ffn), dtype=torch.bfloat16, device=device)
@@ -99,6 +101,22 @@ def decode_chain_step(buf, x, layers, eps=1e-6, fused=True):
             moe_rmsnorm(x, buf.T, buf.shape.hidden, eps, buf.xn)
             decode_layer(buf, buf.xn, w_router, bias, bank, residual=x, out=x)
     return x
+
+
+def decode_chain(buf, x, layers, eps=1e-6, ids=None, w=None):
+    """x <- x + MoE_l(rmsnorm(x)) for every layer, in place, in ONE moe_decode_chain launch.
+
+    layers: list of (w_router, bias, bank) or the ctypes array of ``make_layers``;
+    ids / w: optional [L, T, k] outputs of every layer's route."""
+    if not hasattr(layers, "_type_"):
+        layers = make_layers([(bank, wr, bias) for (wr, bias, bank) in layers])
+    moe_decode_chain(buf.desc, layers, len(layers), x, buf.T, eps, ids, w, buf.ws, buf.ws_bytes)
+    return x
+
+
+def chain_status(buf):
+    """Status word of moe_decode_chain in the workspace (0: no bounded wait expired)."""
+    return int(buf.ws[4:8].view(torch.int32).item())
 
 
 # ---- expert banks from the seeded generator ----------------------------------------------
