@@ -9,8 +9,9 @@ permutation, gate/up GEMV with SwiGLU, down GEMV, combine) over one batch, captu
 HIP graph and replayed.  Inputs and weights are synthetic (seeded generator), resident in HBM
 before the timed region.
 
-Also measured in the same run: the dominant kernel (gate/up GEMV) with HIP events around
-every launch in an eager pass over the same steps (-> achieved GB/s against 8 TB/s); the
+Also measured in the same run: the dominant kernel (gate/up GEMV), launched back to back per
+layer between HIP events (-> achieved GB/s against 8 TB/s); the same stack through the
+single-launch persistent entry point (moe_decode_chain); the
 2,048-token prefill chunk of the same shape through the grouped bf16-MFMA GEMM (-> TFLOP/s
 against the bf16 dense peak); the oracle on the host cores on a bounded sample.
 
@@ -28,6 +29,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published
+COPY_BYTES = 256 << 20         # calibration copy: reads and writes this many bytes
+
+
+def traffic(kernel):
+    from quantized_moe_expert_amd import profiling
+    return profiling.traffic(kernel, ROOT)
 
 
 def log(*a):
@@ -126,43 +133,66 @@ def decode_bench(args):
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # dominant kernel: HIP events around every gate/up launch of eager steps (the layer's three
-    # launches issued as separate stages, on torch's current stream -- the kernels' stream)
-    n_eager = max(1, min(args.steps, args.event_steps))
-    ev, dn_ev = [], []
-    for _ in range(n_eager):
-        x.copy_(x0)
-        for li, (wr, bias, bank) in enumerate(layers):
-            L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=x,
-                                 stages=M.MOE_DECODE_ROUTER)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=x,
+    # dominant kernel (gate/up GEMV): per layer, its router stage once, then `reps` launches of
+    # the gate/up stage back to back between two HIP events on torch's current stream (the
+    # stream the kernels run on); the same for the down stage.  The per-launch average is the
+    # kernel's steady-state duration plus the launch-to-launch gap.
+    reps = args.event_reps
+    gu_ms, dn_ms = [], []
+    x.copy_(x0)
+    for li, (wr, bias, bank) in enumerate(layers):
+        L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=buf.y,
+                             stages=M.MOE_DECODE_ROUTER)
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record()
+        for _ in range(reps):
+            L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=buf.y,
                                  stages=M.MOE_DECODE_GATE_UP)
-            b.record()
-            c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c.record()
-            L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=x,
+        b.record()
+        for _ in range(reps):
+            L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=eps, residual=x, out=buf.y,
                                  stages=M.MOE_DECODE_DOWN)
-            d.record()
-            ev.append((a, b, li))
-            dn_ev.append((c, d, li))
+        c.record()
+        gu_ms.append((a, b))
+        dn_ms.append((b, c))
+        x.copy_(buf.y)
     torch.cuda.synchronize()
-    gu_ms = [a.elapsed_time(b) for (a, b, _) in ev]
-    dn_ms = [c.elapsed_time(d) for (c, d, _) in dn_ev]
+    gu_ms = [a.elapsed_time(b) / reps for (a, b) in gu_ms]
+    dn_ms = [b.elapsed_time(c) / reps for (b, c) in dn_ms]
     gu_avg_ms = sum(gu_ms) / len(gu_ms)
     dn_avg_ms = sum(dn_ms) / len(dn_ms)
-    gu_avg_bytes = sum(gu_bytes[li] for (_, _, li) in ev) / len(ev)
+    gu_avg_bytes = sum(gu_bytes) / len(gu_bytes)
     gu_gbs = gu_avg_bytes / (gu_avg_ms * 1e-3) / 1e9
-    gemv_total_ms = (sum(gu_ms) + sum(dn_ms)) / n_eager
+    gemv_total_ms = sum(gu_ms) + sum(dn_ms)
     gemv_gbs = expert_bytes_step / (gemv_total_ms * 1e-3) / 1e9
+
+    # the same stack in one persistent launch (moe_decode_chain)
+    chain_us = None
+    if T <= 16:
+        arr = M.make_layers([(bank, wr, bias) for (wr, bias, bank) in layers])
+        bufc = L.LayerBuffers(s, T)
+        xc = x0.clone()
+        for _ in range(3):
+            xc.copy_(x0)
+            L.decode_chain(bufc, xc, arr, eps)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_chain = max(1, args.steps // 4)
+        a.record()
+        for _ in range(n_chain):
+            xc.copy_(x0)
+            L.decode_chain(bufc, xc, arr, eps)
+        b.record()
+        torch.cuda.synchronize()
+        chain_us = a.elapsed_time(b) / n_chain * 1e3
+        assert L.chain_status(bufc) == 0, "a bounded wait of the persistent decode expired"
 
     return dict(
         T=T, U=U, ms_step=ms_step, cold_ms=cold_ms,
         tok_s=T / (ms_step * 1e-3),
         gu_avg_us=gu_avg_ms * 1e3, dn_avg_us=dn_avg_ms * 1e3,
         gu_avg_bytes=gu_avg_bytes, gu_gbs=gu_gbs,
-        gemv_gbs=gemv_gbs, expert_bytes_step=expert_bytes_step,
+        gemv_gbs=gemv_gbs, expert_bytes_step=expert_bytes_step, chain_us=chain_us,
         router_bytes_step=router_bytes_step,
         floor_us=(expert_bytes_step + router_bytes_step) / (HBM_PEAK_GBS * 1e9) * 1e6,
         layers=wl.layers, keep=keep)
@@ -282,13 +312,16 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--tokens", type=int, default=1, help="decode batch (1 or 16)")
-    ap.add_argument("--event-steps", type=int, default=20,
-                    help="eager steps timed launch by launch for the dominant kernel")
+    ap.add_argument("--event-reps", type=int, default=20,
+                    help="back-to-back launches a layer timed for the dominant kernel")
     ap.add_argument("--prefill-workload", default="xing4_prefill")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy 3 times (the reference kernel "
+                         "of known traffic for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -301,6 +334,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import quantized_moe_expert_amd as M
     M.lib()
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     d = decode_bench(args)
     log(f"[bench] decode T={d['T']}: {d['ms_step'] * 1e3:.1f} us/step ({d['tok_s']:.1f} tok/s), "
@@ -336,12 +377,15 @@ def main():
             "global_batch": d["T"], "layers": d["layers"], "parallelism": "none (1 GPU)"},
         "roofline": {
             "kernel": "decode_gateup_kernel (routing + IQ4_NL dequant-GEMV gate/up + SwiGLU)",
+            "bytes_note": "active experts' gate+up IQ4_NL bytes + activations in + h out",
             "bound": "hbm",
             "achieved": round(d["gu_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(d["gu_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic("decode_gateup_kernel"),
+            "traffic_note": "HBM bytes a launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from "
+                            "profiles/pmc_traffic_xing4.txt; null if the kernel changed since",
             "bytes_per_launch": round(d["gu_avg_bytes"]),
             "avg_launch_us": round(d["gu_avg_us"], 3),
         },
@@ -354,6 +398,7 @@ def main():
             "gemv_expert_GBps": round(d["gemv_gbs"], 1),
             "gemv_expert_frac_of_hbm": round(d["gemv_gbs"] / HBM_PEAK_GBS, 4),
             "down_avg_launch_us": round(d["dn_avg_us"], 3),
+            "persistent_chain_us_per_step": (round(d["chain_us"], 2) if d["chain_us"] else None),
         },
     }
     if p:
@@ -366,6 +411,8 @@ def main():
             "layer_tok_s": round(p["T"] / (p["layer_ms"] * 1e-3), 1),
             "flop_per_layer": p["flop"],
             "expert_load_max_over_mean": round(p["load_max_over_mean"], 2),
+            "gate_up_traffic_bytes": traffic("gemm_kernel<true>"),
+            "down_traffic_bytes": traffic("gemm_kernel<false>"),
         }
     if cpu:
         rec["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}

@@ -1,0 +1,119 @@
+"""Summaries of rocprofv3 output for the profiles/ folder, and the HBM traffic they record.
+
+``python -m quantized_moe_expert_amd.profiling stats KERNEL_STATS_CSV "COMMAND" > out.txt``
+    a short text table of a ``--kernel-trace --stats`` run (the kernels' average durations).
+``python -m quantized_moe_expert_amd.profiling pmc FETCH_CSV WRITE_CSV "COMMANDS" > out.txt``
+    per-kernel FETCH_SIZE / WRITE_SIZE (KiB a dispatch) of two ``--pmc`` runs, scaled by what
+    the same counters read for the plain 256 MiB device copy that ``bench.py
+    --copy-calibration`` runs first (its true traffic is known: 256 MiB read, 256 MiB written),
+    with a digest of the kernel sources the numbers belong to.
+
+``traffic(kernel, root)`` reads such a summary back (bench.py's ``roofline.traffic``) and
+returns None when the sources have changed since the counters were taken.
+"""
+import csv
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+COPY_BYTES = 256 << 20
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# sources each profiled kernel is compiled from
+KERNEL_SOURCES = {
+    "decode_gateup_kernel": ("decode.hip", "gemv_core.h", "common.h", "route_core.h", "kernels.h"),
+    "decode_down_combine_kernel": ("decode.hip", "gemv_core.h", "common.h", "kernels.h"),
+    "gemm_kernel<true>": ("gemm.hip", "common.h", "kernels.h"),
+    "gemm_kernel<false>": ("gemm.hip", "common.h", "kernels.h"),
+}
+PMC_FILE = "pmc_traffic_xing4.txt"
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name):
+    m = re.search(r"(\w+_kernel(<[^>]*>)?|__amd_rocclr_\w+)", name)
+    return m.group(1) if m else name[:60]
+
+
+def stats_summary(stats_csv, command):
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"command: {command}", "",
+           f"{'calls':>7} {'avg us':>10} {'min us':>10} {'max us':>10} {'% time':>7}  kernel"]
+    for r in rows[:16]:
+        out.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                   f"{float(r['Percentage']):7.2f}  {r['Name'][:110]}")
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel(path, counter):
+    vals = defaultdict(list)
+    calib = None
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        if calib is None and "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 131072:
+            calib = float(r["Counter_Value"])            # first dispatch: the 256 MiB copy
+        vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return vals, calib
+
+
+def _source_key(short):
+    if short in KERNEL_SOURCES:
+        return short
+    base = short.split("<")[0]
+    return base if base in KERNEL_SOURCES else None
+
+
+def pmc_summary(fetch_csv, write_csv, commands):
+    fetch, cf = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write, cw = _per_kernel(write_csv, "WRITE_SIZE")
+    if not cf or not cw:
+        raise SystemExit("no calibration copy found (run bench.py with --copy-calibration)")
+    sf = COPY_BYTES / (cf * 1024)
+    sw = COPY_BYTES / (cw * 1024)
+    out = [f"commands: {commands}", "",
+           f"calibration: 256 MiB device copy reads FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB",
+           f"scale: fetch x{sf:.4f}, write x{sw:.4f} (true bytes / counter bytes)", ""]
+    for k in sorted(set(fetch) & set(write)):
+        f = sum(fetch[k]) / len(fetch[k]) * 1024 * sf
+        w = sum(write[k]) / len(write[k]) * 1024 * sw
+        line = f"kernel {k}: dispatches {len(fetch[k])}: fetch_bytes {f:.0f} write_bytes {w:.0f}"
+        key = _source_key(k)
+        if key:
+            line += f" source_digest {source_digest(key)}"
+        out.append(line)
+    return "\n".join(out) + "\n"
+
+
+def traffic(kernel, root):
+    """HBM bytes a dispatch (fetch + write) recorded for `kernel`, or None if missing/stale."""
+    path = os.path.join(root, "profiles", PMC_FILE)
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"^kernel (.+): dispatches \d+: fetch_bytes (\d+) write_bytes (\d+)"
+                     r" source_digest (\w+)")
+    for line in open(path):
+        m = pat.match(line.strip())
+        if m and _source_key(m.group(1)) == kernel:
+            if m.group(4) != source_digest(kernel):
+                return None
+            return int(m.group(2)) + int(m.group(3))
+    return None
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        sys.stdout.write(stats_summary(sys.argv[2], sys.argv[3]))
+    elif sys.argv[1] == "pmc":
+        sys.stdout.write(pmc_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
+    else:
+        raise SystemExit(__doc__)
