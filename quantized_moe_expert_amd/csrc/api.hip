@@ -78,7 +78,7 @@ size_t logits_bytes(const moe_desc* d, int32_t T) { return align256((size_t)T * 
 // Fused decode layer: header | logits | rscale | ids | w | offsets | sorted_pairs | pair_slot |
 // h | o (o only when down + combine cannot be fused).
 struct DecodeLayout {
-  size_t logits, rscale, ids, w, offsets, sp, ps, h, o, total;
+  size_t logits, rscale, ids, w, offsets, sp, ps, h, xn, o, total;
 };
 
 DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
@@ -94,8 +94,10 @@ DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
   L.sp = off; off += align256(P * 4);
   L.ps = off; off += align256(P * 4);
   L.h = off; off += align256(rows * d->ffn * 4);
+  L.xn = off; off += align256((size_t)T * d->hidden * 4);
   L.o = off;
-  if (!moe::decode_down_fused_fits(Shape{d->hidden, d->ffn, d->n_experts, d->top_k,
+  if (T > moe::kDecodeFusedMaxT ||
+      !moe::decode_down_fused_fits(Shape{d->hidden, d->ffn, d->n_experts, d->top_k,
                                          d->n_shared, d->gating, d->renormalize}, T))
     off += align256(rows * d->hidden * 4);
   L.total = off;
@@ -317,6 +319,8 @@ moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
   sc.o = reinterpret_cast<float*>(b + L.o);
+  sc.xn = reinterpret_cast<float*>(b + L.xn);
+  sc.count = reinterpret_cast<int32_t*>(b);
   return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
                                              w_router, bias, x, n_tokens, norm_eps, residual, y,
                                              sc, stages, stream));
@@ -372,6 +376,8 @@ moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
   sc.o = reinterpret_cast<float*>(b + L.o);
+  sc.xn = reinterpret_cast<float*>(b + L.xn);
+  sc.count = reinterpret_cast<int32_t*>(b);
   for (int32_t l = 0; l < n_layers; ++l) {
     sc.ids = topk_ids ? topk_ids + l * P : reinterpret_cast<int32_t*>(b + L.ids);
     sc.w = topk_w ? topk_w + l * P : reinterpret_cast<float*>(b + L.w);

@@ -26,10 +26,6 @@ namespace moe {
 constexpr int kDecThreads = 256;
 constexpr int kDecMaxT = 16;
 constexpr int kDecMaxK = 32;
-#ifndef MOE_DECODE_UP_PASSES
-#define MOE_DECODE_UP_PASSES 8
-#endif
-constexpr int kUpPasses = MOE_DECODE_UP_PASSES;   // weight rows a lane group visits (even)
 constexpr int kDownRing = 16;       // passes in flight in the down kernel
 constexpr int kDownStageUnits = 12; // staging units a thread: rows * F/32 * 4 <= 3072
 
@@ -122,13 +118,15 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
 
 // ---- gate/up with in-workgroup routing -------------------------------------------------
 
-template <int LPR, int BPL, int MT>
+// PASSES: weight rows a lane group visits (even: gate rows, then the matching up rows).
+template <int LPR, int BPL, int MT, int kUpPasses>
 __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const float* __restrict__ x,
     const float* __restrict__ rscale, const float* __restrict__ logits, int T, int H, int F,
     int E, int S, int k, int gating, int renorm, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, int32_t* __restrict__ offsets_out,
-    int32_t* __restrict__ sp_out, int32_t* __restrict__ ps_out, float* __restrict__ h_out) {
+    int32_t* __restrict__ sp_out, int32_t* __restrict__ ps_out, float* __restrict__ h_out,
+    int tch) {
   constexpr int RPP = 64 / LPR;
   constexpr int WROWS = kUpPasses * RPP;
   constexpr int OROWS = WROWS / 2;
@@ -144,6 +142,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * k, NBIN = E + S;
+  const int nch = (T + tch - 1) / tch;             // token chunks an expert is split into
   s_tab[tid] = pair_table_entry(tid);
   for (int i = tid; i < 1024; i += kDecThreads) s_cnt[i] = 0;
   for (int t = wave; t < T; t += 4)
@@ -155,7 +154,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
 
   // the blockIdx.y-th expert with routes, and the number of slots before it
   if (wave == 0) {
-    const int target = blockIdx.y;
+    const int target = blockIdx.y / nch;
     int seen = 0, run = 0, found = -1, slot0 = 0;
     for (int base = 0; base < NBIN && found < 0; base += 64) {
       const int b = base + lane;
@@ -182,7 +181,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   __syncthreads();
   const int e = s_e;
   if (e < 0) return;
-  const int slot0 = s_slot0, m = s_m;
+  const int slot0 = s_slot0;
+  // this workgroup's share of the expert's tokens: [tb, tb + m)
+  const int tb = (blockIdx.y % nch) * tch;
+  if (tb >= s_m) return;
+  const int m = min(tch, s_m - tb);
 
   // tokens of expert e, in pair order
   if (wave == 0) {
@@ -207,8 +210,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   const int NB = H >> 5;
   Stager<4 * MT> stg;
   stg.load(NB, LPR * BPL, min(MT, m), MT,
-           [&](int u) -> const float* { return x + (int64_t)s_tok[u] * H; },
-           [&](int u) { return rscale ? rscale[s_tok[u]] : 1.0f; });
+           [&](int u) -> const float* { return x + (int64_t)s_tok[tb + u] * H; },
+           [&](int u) { return rscale ? rscale[s_tok[tb + u]] : 1.0f; });
   // weight loads of this wave (rows stay in registers for every token tile)
   const int64_t row_bytes = (int64_t)NB * kBlockBytes;
   const uint8_t* mat = bank + (int64_t)e * stride;
@@ -272,8 +275,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
     if (t0) {
       lds_barrier();
       stg.load(NB, LPR * BPL, n_tok, MT,
-               [&](int u) -> const float* { return x + (int64_t)s_tok[t0 + u] * H; },
-               [&](int u) { return rscale ? rscale[s_tok[t0 + u]] : 1.0f; });
+               [&](int u) -> const float* { return x + (int64_t)s_tok[tb + t0 + u] * H; },
+               [&](int u) { return rscale ? rscale[s_tok[tb + t0 + u]] : 1.0f; });
     }
     stg.store(s_x);
     lds_barrier();
@@ -287,7 +290,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
         if (u >= n_tok) continue;
-        const int64_t s = slot0 + t0 + u;
+        const int64_t s = slot0 + tb + t0 + u;
 #pragma unroll
         for (int p = 0; p < kUpPasses / 2; ++p) {
           const int r = orow0 + p * RPP + g;
@@ -450,24 +453,24 @@ bool decode_down_fused_fits(const Shape& sh, int T) {
          rows_total * nbp * 4 <= kDecThreads * kDownStageUnits;
 }
 
-template <int LPR, int BPL, int MT>
+template <int LPR, int BPL, int MT, int P>
 static void launch_up(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t stride,
                       const float* x, const float* rs, const float* logits, int T,
                       const Shape& sh, int32_t* ids, float* w, int32_t* off, int32_t* sp,
-                      int32_t* ps, float* h) {
+                      int32_t* ps, float* h, int tch) {
   const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
-  hipLaunchKernelGGL((decode_gateup_kernel<LPR, BPL, MT>), grid, dim3(kDecThreads), lds, s, bank,
-                     stride, x, rs, logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating,
-                     sh.renorm, ids, w, off, sp, ps, h);
+  hipLaunchKernelGGL((decode_gateup_kernel<LPR, BPL, MT, P>), grid, dim3(kDecThreads), lds, s,
+                     bank, stride, x, rs, logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating,
+                     sh.renorm, ids, w, off, sp, ps, h, tch);
 }
 
-template <int MT>
+template <int MT, int P>
 static bool dispatch_up(DecGeom gm, dim3 grid, hipStream_t s, const uint8_t* bank,
                         int64_t stride, const float* x, const float* rs, const float* logits,
                         int T, const Shape& sh, int32_t* ids, float* w, int32_t* off,
                         int32_t* sp, int32_t* ps, float* h) {
 #define UP(L, B) \
-  if (gm.lpr == L && gm.bpl == B) { launch_up<L, B, MT>(grid, s, bank, stride, x, rs, logits, T, sh, ids, w, off, sp, ps, h); return true; }
+  if (gm.lpr == L && gm.bpl == B) { launch_up<L, B, MT, P>(grid, s, bank, stride, x, rs, logits, T, sh, ids, w, off, sp, ps, h, T); return true; }
   UP(64, 1) UP(64, 2) UP(64, 3) UP(64, 4) UP(32, 1) UP(32, 2) UP(32, 3) UP(32, 4)
   UP(16, 1) UP(16, 2) UP(16, 3) UP(16, 4) UP(8, 1) UP(8, 2) UP(4, 1) UP(4, 2)
 #undef UP
@@ -530,24 +533,65 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   if (T == 0) return hipSuccess;
   const int use_norm = eps >= 0.0f ? 1 : 0;
   hipError_t err = hipSuccess;
+  if (T > kDecodeFusedMaxT) {
+    // several tokens: route once (rows normalised into xn), then the slot-chunked GEMVs
+    const float* xin = x;
+    if (stages & 1) {
+      if (use_norm) {
+        err = launch_rmsnorm(x, T, sh.H, eps, sc.xn, s);
+        if (err != hipSuccess) return err;
+      }
+      xin = use_norm ? sc.xn : x;
+      err = launch_router_rows(sh, xin, wr, bias, T, -1.0f, sc.logits, nullptr, s);
+      if (err != hipSuccess) return err;
+      err = launch_topk(sh, sc.logits, T, sc.ids, sc.w, s);
+      if (err != hipSuccess) return err;
+      err = launch_permute(sh, sc.ids, sc.w, T, nullptr, nullptr, 0, sc.offsets, sc.sorted_pairs,
+                           sc.pair_slot, sc.count, nullptr, s);
+      if (err != hipSuccess) return err;
+    }
+    xin = use_norm ? sc.xn : x;
+    if (stages & 2) {
+      err = launch_gemv(sh, 0, bank, stride, sc.offsets, sc.sorted_pairs, xin, sc.h, T, s);
+      if (err != hipSuccess) return err;
+    }
+    if (stages & 4) {
+      err = launch_gemv(sh, 1, bank, stride, sc.offsets, nullptr, sc.h, sc.o, T, s);
+      if (err != hipSuccess) return err;
+      err = launch_combine(sh, sc.o, sc.pair_slot, sc.w, T, residual, y, s);
+    }
+    return err;
+  }
   if (stages & 1) {
     err = launch_router_rows(sh, x, wr, bias, T, eps, sc.logits, sc.rscale, s);
     if (err != hipSuccess) return err;
   }
   if (stages & 2) {
 
-  // gate/up with routing
-  const DecGeom gu = dec_geom(sh.H / 32);
+  // gate/up with routing.  One token: 4 passes of the least-waste geometry.  Several
+  // tokens: when the row splits exactly into 16 lanes x 7 blocks (hidden 3584), 2 passes of
+  // that geometry (smaller workgroups, so the shared expert's token tiles spread wider).
+  const int nb = sh.H / 32;
+  const bool wide = T > 1 && nb == 112;
+  const DecGeom gu = wide ? DecGeom{16, 7} : dec_geom(nb);
   if (gu.lpr == 0) return hipErrorInvalidValue;
-  const int orows_wg = (kDecThreads / 64) * kUpPasses * (64 / gu.lpr) / 2;
+  const int passes = wide ? 2 : 4;
+  const int orows_wg = (kDecThreads / 64) * passes * (64 / gu.lpr) / 2;
   const int max_active = (int)std::min<int64_t>(sh.E, (int64_t)T * sh.k) + sh.S;
-  dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active);
+  const int tch = T;                               // every token of an expert in one workgroup
+  dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active * ((T + tch - 1) / tch));
   const float* rs = use_norm ? sc.rscale : nullptr;
-  const bool ok = (T > 1 && gu.bpl <= 2)
-      ? dispatch_up<2>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
-                       sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h)
-      : dispatch_up<1>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
-                       sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
+  bool ok;
+  if (wide) {
+    launch_up<16, 7, 2, 2>(grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h, tch);
+    ok = true;
+  } else if (T > 1 && gu.bpl <= 2)
+    ok = dispatch_up<2, 4>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
+  else
+    ok = dispatch_up<1, 4>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
   if (!ok) return hipErrorInvalidValue;
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -26,6 +26,7 @@ constexpr int kBN = 128;               // weight rows per tile
 constexpr int kKB = 4;                 // IQ4_NL blocks per K step (128 k)
 constexpr int kLdsStride = kKB * 16 + 4;   // dwords per LDS row (bf16 pairs + pad)
 constexpr int kGemmThreads = 256;
+constexpr int kXcds = 8;               // XCDs of an MI355X (each with its own L2)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -83,7 +84,16 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
   const int64_t row_bytes = (int64_t)NB * kBlockBytes;
   const int64_t mat_off = GATEUP ? 0 : 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
 
-  for (int tile = blockIdx.x; tile < total_m * NT; tile += gridDim.x) {
+  // XCD-aware walk: workgroup b runs on XCD b % 8 (dispatch is round-robin over the XCDs);
+  // each XCD takes one contiguous range of the tile list, so the workgroups sharing an
+  // activation tile (same M tile, consecutive N tiles) and a weight tile (same expert and N
+  // tile) meet in the same L2.
+  const int n_tiles = total_m * NT;
+  const int n_xcd = gridDim.x % kXcds == 0 ? kXcds : 1;
+  const int xcd = blockIdx.x % n_xcd, wix = blockIdx.x / n_xcd, nw = gridDim.x / n_xcd;
+  const int per_xcd = (n_tiles + n_xcd - 1) / n_xcd;
+  const int t_end = min(n_tiles, (xcd + 1) * per_xcd);
+  for (int tile = xcd * per_xcd + wix; tile < t_end; tile += nw) {
     const int mt = tile / NT, nt = tile % NT;
     // expert owning M-tile mt: first e with s_pref[e] > mt
     int lo = 0, hi = nbins - 1;
@@ -135,26 +145,24 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int kt = 0; kt < NKT; ++kt) {
-      // global loads for this K step
-      uint4 ga[4][2];
+    // K loop, software-pipelined: the global loads of step kt+1 are in flight while the
+    // MFMAs of step kt run; barriers order LDS only, so they do not wait for those loads.
+    uint4 ga[4][2];
+    RawBlock gb[2];
+    auto gload = [&](int kt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint16_t* src = arow[i] + (kt * kKB + ak[i]) * 32 + 8 * ac[i];
-        if (aok[i]) {
-          ga[i][0] = *reinterpret_cast<const uint4*>(src);
-          ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
-        } else {
-          ga[i][0] = make_uint4(0, 0, 0, 0);
-          ga[i][1] = make_uint4(0, 0, 0, 0);
-        }
+        ga[i][0] = *reinterpret_cast<const uint4*>(src);
+        ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
       }
-      RawBlock gb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) gb[i] = load_block(brow[i], kt * kKB + bk[i]);
-
-      __syncthreads();   // everyone is done reading the previous tile
-      // A -> LDS in pair order: dword j = (a[j], a[j+16])
+    };
+    gload(0);
+    for (int kt = 0; kt < NKT; ++kt) {
+      lds_barrier();     // every wave is done reading the previous step's tiles
+      // A -> LDS in pair order: dword j = (a[j], a[j+16]); rows past the expert's end are 0
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t a0[4] = {ga[i][0].x, ga[i][0].y, ga[i][0].z, ga[i][0].w};
@@ -162,8 +170,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
         uint32_t d[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          d[2 * w] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
-          d[2 * w + 1] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+          d[2 * w] = aok[i] ? __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u) : 0u;
+          d[2 * w + 1] = aok[i] ? __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u) : 0u;
         }
         uint4* dst = reinterpret_cast<uint4*>(&sA[ar[i] * kLdsStride + ak[i] * 16 + 8 * ac[i]]);
         dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
@@ -190,7 +198,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
         dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
         dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
       }
-      __syncthreads();
+      if (kt + 1 < NKT) gload(kt + 1);
+      lds_barrier();
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         bf16x8_t af[4], bfr[4];

@@ -57,7 +57,7 @@ template <int LPR, int BPL, int MT, bool GATEUP>
 __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ in,
-    float* __restrict__ out, int H, int F, int E, int S, int k, int T) {
+    float* __restrict__ out, int H, int F, int E, int S, int k, int T, int tch) {
   constexpr int RPP = 64 / LPR;               // rows per pass per wave
   constexpr int WROWS = kPasses * RPP;        // weight rows per wave
   constexpr int OROWS = GATEUP ? WROWS / 2 : WROWS;
@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   const int tid = threadIdx.x;
   s_tab[tid] = pair_table_entry(tid);
   if (tid < 64) {
-    const int e = find_active_expert(offsets, E + S, blockIdx.y);
+    const int e = find_active_expert(offsets, E + S, blockIdx.y / ((T + tch - 1) / tch));
     if (tid == 0) s_expert = e;
   }
   __syncthreads();
@@ -84,8 +84,13 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   const uint8_t* wbase = bank + (int64_t)e * stride;
   const uint8_t* mat = GATEUP ? wbase : wbase + 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
 
-  const int slot0 = offsets[e];
-  const int m = offsets[e + 1] - slot0;
+  // this workgroup's chunk of the expert's slots (an expert with many tokens is spread over
+  // several workgroups, each streaming the weights once for its chunk)
+  const int tb = (blockIdx.y % ((T + tch - 1) / tch)) * tch;
+  const int m_all = offsets[e + 1] - offsets[e];
+  if (tb >= m_all) return;
+  const int slot0 = offsets[e] + tb;
+  const int m = min(tch, m_all - tb);
   const int P = T * k;
 
   const int wave = tid >> 6, lane = tid & 63;
@@ -210,8 +215,10 @@ static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t st
                        const int32_t* offsets, const int32_t* sp, const float* in, float* out,
                        const Shape& sh, int T) {
   const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
+  const int tch = (T > 4 && T <= 16) ? 4 : T;   // slots a workgroup takes of one expert
+  grid.y *= (T + tch - 1) / tch;
   hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,
-                     stride, offsets, sp, in, out, sh.H, sh.F, sh.E, sh.S, sh.k, T);
+                     stride, offsets, sp, in, out, sh.H, sh.F, sh.E, sh.S, sh.k, T, tch);
 }
 
 template <int LPR, int MT, bool GU>

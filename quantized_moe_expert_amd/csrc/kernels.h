@@ -16,6 +16,8 @@ hipError_t launch_dequantize(const uint8_t* blk, int64_t n_blocks, float* out, h
 
 hipError_t launch_route(const Shape& sh, const float* x, const float* wr, const float* bias,
                         int T, int32_t* ids, float* w, float* logits, hipStream_t s);
+hipError_t launch_topk(const Shape& sh, const float* logits, int T, int32_t* ids, float* w,
+                       hipStream_t s);
 
 // scratch: workspace region for the permutation (size from permute_scratch_bytes)
 size_t permute_scratch_bytes(const Shape& sh, int T);
@@ -48,10 +50,15 @@ struct DecodeScratch {
   int32_t* sorted_pairs;  // [T * k]
   int32_t* pair_slot;     // [T * k]
   float* h;               // [rows, F]
-  float* o;               // [rows, H] (only when down + combine cannot be fused)
+  float* o;               // [rows, H] (only when down + combine are separate launches)
+  float* xn;              // [T, H] normalised input (batches above kDecodeFusedMaxT)
+  int32_t* count;         // sanitised-pair count of the permutation
 };
 
 constexpr int kDecodeMaxTokens = 16;
+// Up to this many tokens a decode layer routes inside its gate/up workgroups (three
+// launches); above it the route, permutation, GEMVs and combine are separate launches.
+constexpr int kDecodeFusedMaxT = 4;
 // logits (and, with eps >= 0, the RMSNorm scale of each row) for T <= 16 rows
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,

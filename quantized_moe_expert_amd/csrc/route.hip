@@ -79,6 +79,14 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   wave_topk(logits + (size_t)t * E, E, k, gating, renorm, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
+hipError_t launch_topk(const Shape& sh, const float* logits, int T, int32_t* ids, float* w,
+                       hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, sh.E, sh.k,
+                     sh.gating, sh.renorm, ids, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const Shape& sh, const float* x, const float* wr, const float* bias,
                         int T, int32_t* ids, float* w, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
@@ -91,9 +99,7 @@ hipError_t launch_route(const Shape& sh, const float* x, const float* wr, const 
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, sh.E, sh.k,
-                     sh.gating, sh.renorm, ids, w);
-  return hipGetLastError();
+  return launch_topk(sh, logits, T, ids, w, s);
 }
 
 }  // namespace moe
