@@ -129,7 +129,10 @@ ChainLayout chain_layout(const moe_desc* d, int32_t T) {
 }
 
 size_t ws_bytes_for(const moe_desc* d, int32_t T) {
-  size_t b = kHeaderBytes + logits_bytes(d, T) + align256(moe::permute_scratch_bytes(shape_of(d), T));
+  const size_t route_part = (size_t)moe::route_splits(shape_of(d), T, ~size_t(0)) * T *
+                           d->n_experts * 4;
+  size_t b = kHeaderBytes + logits_bytes(d, T) +
+             align256(std::max(moe::permute_scratch_bytes(shape_of(d), T), route_part));
   if (T <= moe::kDecodeMaxTokens) {
     b = std::max(b, decode_layout(d, T).total);
     b = std::max(b, chain_layout(d, T).total);
@@ -210,8 +213,16 @@ moe_status moe_route(const moe_desc* desc, const float* x, const float* w_router
     if (ws_bytes < kHeaderBytes + logits_bytes(desc, n_tokens)) return MOE_ERR_WORKSPACE;
     logits = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kHeaderBytes);
   }
+  // split-K partial logits in the workspace after the logits, when it has room (else no split)
+  float* partial = nullptr;
+  size_t partial_floats = 0;
+  const size_t base = kHeaderBytes + logits_bytes(desc, n_tokens);
+  if (ws && aligned(ws, 256) && ws_bytes > base) {
+    partial = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + base);
+    partial_floats = (ws_bytes - base) / 4;
+  }
   return hip_status(moe::launch_route(shape_of(desc), x, w_router, bias, n_tokens, topk_ids,
-                                      topk_w, logits, stream));
+                                      topk_w, logits, partial, partial_floats, stream));
 }
 
 moe_status moe_permute(const moe_desc* desc, int32_t* topk_ids, float* topk_w,

@@ -14,8 +14,11 @@ struct Shape {
 hipError_t launch_quantize(const float* w, int64_t n_blocks, uint8_t* out, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* blk, int64_t n_blocks, float* out, hipStream_t s);
 
+// partial: scratch for the split-K partial logits (partial_floats floats; NULL: no split)
 hipError_t launch_route(const Shape& sh, const float* x, const float* wr, const float* bias,
-                        int T, int32_t* ids, float* w, float* logits, hipStream_t s);
+                        int T, int32_t* ids, float* w, float* logits, float* partial,
+                        size_t partial_floats, hipStream_t s);
+int route_splits(const Shape& sh, int T, size_t cap_floats);
 hipError_t launch_topk(const Shape& sh, const float* logits, int T, int32_t* ids, float* w,
                        hipStream_t s);
 
