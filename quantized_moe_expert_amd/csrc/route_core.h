@@ -3,7 +3,8 @@
 // Selection (PocketLLM "Xing4.0-29B-A4B", "Overview": top-4 of 64 sigmoid-routed experts;
 // Red Lite "1. The idea": 10 of 512; Xolotl "Why build an engine at all": 6 of 384): the k
 // largest logits in descending order, ties to the lower expert index, NaN below every
-// number.  k rounds of a wave-wide maximum over the 64-bit key (order_bits(logit), ~index).
+// number.  k rounds of a wave-wide maximum of the order-preserving logit bits, then the
+// lowest expert index among the lanes holding that maximum (DPP reductions).
 #pragma once
 #include "common.h"
 
@@ -18,49 +19,80 @@ __device__ __forceinline__ uint32_t order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_max_f(float v) {
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
 constexpr int kMaxE = 1024;
-constexpr int kKeysPerLane = kMaxE / 64;
+
+// Wave-wide max / min of a 32-bit unsigned value and max of a float: a DPP butterfly inside
+// each row of 16 lanes, then the four row results read back with readlane (no LDS round trip).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppXor2, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xF, 0xF, false));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  const int iv = __builtin_bit_cast(int, v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// KPL logits a lane (experts lane + 64 i).  Each round: the wave-wide largest key (order bits
+// + 1, so that a NaN logit, key 1, stays selectable and 0 marks "taken / absent"), then the
+// lowest expert index among the lanes holding it.
+template <int KPL>
+__device__ __forceinline__ int wave_select(const float* __restrict__ l, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? order_bits(l[e]) + 1u : 0u;
+  }
+  int my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    uint32_t b = 0;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (key[i] > b) { b = key[i]; bi = i; }             // strict: the lower index wins ties
+    const uint32_t m = wave_max_u32(b);
+    const uint32_t cand = (b == m && b != 0u) ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu;
+    const int e = (int)wave_min_u32(cand);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (lane + 64 * i == e) key[i] = 0u;
+    if (lane == j) my_e = e;
+  }
+  return my_e;
+}
 
 // ids[0..k-1], w[0..k-1] of one token's logits l[0..E-1] (E <= 1024, k <= 32); all 64
 // lanes of the wave take part; lanes j < k write entry j.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int k, int gating,
                                           int renorm, int32_t* ids, float* w) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[kKeysPerLane];
-#pragma unroll
-  for (int i = 0; i < kKeysPerLane; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)order_bits(l[e]) << 32) | (uint32_t)(0xFFFFFFFFu - e)) : 0ull;
-  }
-  int my_e = -1;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if ((e & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < kKeysPerLane; ++i)
-        if (i == (e >> 6)) key[i] = 0ull;
-    }
-    if (lane == j) my_e = e;
-  }
+  int my_e;
+  if (E <= 64) my_e = wave_select<1>(l, E, k);
+  else if (E <= 128) my_e = wave_select<2>(l, E, k);
+  else if (E <= 256) my_e = wave_select<4>(l, E, k);
+  else if (E <= 512) my_e = wave_select<8>(l, E, k);
+  else my_e = wave_select<16>(l, E, k);
   const bool mine = lane < k;
   const float v = mine ? l[my_e] : 0.0f;
   float s;
@@ -72,11 +104,11 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, in
     m = wave_max_f(m);
     float z = 0.0f;
     for (int e = lane; e < E; e += 64) z += expf(l[e] - m);
-    z = group_sum(z, 64);
+    z = group_sum_dpp<64>(z);
     s = mine ? expf(v - m) / z : 0.0f;
   }
   if (renorm) {
-    const float tot = group_sum(s, 64);
+    const float tot = group_sum_dpp<64>(s);
     s = s / tot;
   }
   if (mine) {
