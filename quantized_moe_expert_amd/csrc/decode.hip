@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   const int P = T * k, NBIN = E + S;
   const int nch = (T + tch - 1) / tch;             // token chunks an expert is split into
   s_tab[tid] = pair_table_entry(tid);
-  for (int i = tid; i < 1024; i += kDecThreads) s_cnt[i] = 0;
+  for (int i = tid; i < NBIN; i += kDecThreads) s_cnt[i] = 0;
   for (int t = wave; t < T; t += 4)
     wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
   __syncthreads();
@@ -165,11 +165,12 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
         uint64_t mm = mask;
         for (int i = 0; i < target - seen; ++i) mm &= mm - 1;
         const int pos = __ffsll((long long)mm) - 1;
-        slot0 = run + group_sum_int(lane < pos ? c : 0, 64);
+        // slot counts are small integers: exact as float sums
+        slot0 = run + (int)group_sum_dpp<64>((float)(lane < pos ? c : 0));
         found = base + pos;
       } else {
         seen += cnt;
-        run += group_sum_int(c, 64);
+        run += (int)group_sum_dpp<64>((float)c);
       }
     }
     if (lane == 0) {
