@@ -32,25 +32,33 @@ constexpr int kGemvThreads = 256;
 #endif
 constexpr int kPasses = MOE_GEMV_PASSES;   // weight rows a lane group visits (even)
 
-// e_slot-th expert (0-based, in index order) whose slot range is non-empty; -1 if none.
-__device__ int find_active_expert(const int32_t* __restrict__ offsets, int n_bins, int e_slot) {
+// Work item `item` of the list of (expert, chunk of tch slots) pairs over the experts with
+// slots, in index order: e (-1 past the end) and the chunk index.  One wave.
+__device__ void find_work(const int32_t* __restrict__ offsets, int n_bins, int item, int tch,
+                          int& e_out, int& chunk_out) {
   const int lane = threadIdx.x & 63;
-  int seen = 0;
+  int before = 0;
   for (int base = 0; base < n_bins; base += 64) {
-    const int e = base + lane;
-    const bool ne = e < n_bins && offsets[e + 1] > offsets[e];
-    const uint64_t mask = __ballot(ne);
-    const int cnt = __popcll(mask);
-    if (e_slot < seen + cnt) {
-      // position of the (e_slot - seen)-th set bit
-      int want = e_slot - seen;
-      uint64_t m = mask;
-      for (int i = 0; i < want; ++i) m &= m - 1;
-      return base + __ffsll((long long)m) - 1;
+    const int b = base + lane;
+    const int c = b < n_bins ? (offsets[b + 1] - offsets[b] + tch - 1) / tch : 0;
+    int incl = c;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
     }
-    seen += cnt;
+    const int total = __shfl(incl, 63, 64);
+    if (item < before + total) {
+      const int lo = before + incl - c;
+      const uint64_t mask = __ballot(item >= lo && item < lo + c);
+      const int hl = __ffsll((long long)mask) - 1;
+      e_out = base + hl;
+      chunk_out = item - __shfl(lo, hl, 64);
+      return;
+    }
+    before += total;
   }
-  return -1;
+  e_out = -1;
+  chunk_out = 0;
 }
 
 template <int LPR, int BPL, int MT, bool GATEUP>
@@ -63,14 +71,18 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   constexpr int OROWS = GATEUP ? WROWS / 2 : WROWS;
   extern __shared__ uint32_t s_x[];           // MT tokens x LPR*BPL blocks x kXStride dwords
   __shared__ uint32_t s_tab[256];
-  __shared__ int s_expert;
+  __shared__ int s_expert, s_chunk;
   __shared__ int s_row[MT];                   // row index of each staged token in `in`
 
   const int tid = threadIdx.x;
   s_tab[tid] = pair_table_entry(tid);
   if (tid < 64) {
-    const int e = find_active_expert(offsets, E + S, blockIdx.y / ((T + tch - 1) / tch));
-    if (tid == 0) s_expert = e;
+    int e, c;
+    find_work(offsets, E + S, blockIdx.y, tch, e, c);
+    if (tid == 0) {
+      s_expert = e;
+      s_chunk = c;
+    }
   }
   __syncthreads();
   const int e = s_expert;
@@ -86,7 +98,7 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
 
   // this workgroup's chunk of the expert's slots (an expert with many tokens is spread over
   // several workgroups, each streaming the weights once for its chunk)
-  const int tb = (blockIdx.y % ((T + tch - 1) / tch)) * tch;
+  const int tb = s_chunk * tch;
   const int m_all = offsets[e + 1] - offsets[e];
   if (tb >= m_all) return;
   const int slot0 = offsets[e] + tb;
@@ -215,8 +227,11 @@ static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t st
                        const int32_t* offsets, const int32_t* sp, const float* in, float* out,
                        const Shape& sh, int T) {
   const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
-  const int tch = (T > 4 && T <= 16) ? 4 : T;   // slots a workgroup takes of one expert
-  grid.y *= (T + tch - 1) / tch;
+  // slots a workgroup takes of one expert; work items: (expert, chunk), at most one partial
+  // chunk an expert beyond rows / tch
+  const int tch = (T > 4 && T <= 16) ? 4 : T;
+  const int rows = T * (sh.k + sh.S);
+  grid.y += (rows + tch - 1) / tch;
   hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,
                      stride, offsets, sp, in, out, sh.H, sh.F, sh.E, sh.S, sh.k, T, tch);
 }
