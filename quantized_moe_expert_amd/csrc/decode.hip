@@ -31,7 +31,9 @@ constexpr int kDownStageUnits = 12; // staging units a thread: rows * F/32 * 4 <
 
 // ---- router --------------------------------------------------------------------------
 
-template <int EPW>
+// KM: float4 a thread of one W_r row (ceil(H / 1024)).  Tokens are processed in groups of TG
+// whose activation loads are issued together.
+template <int EPW, int KM, int TG>
 __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int H, int E, float eps, int use_norm, float* __restrict__ logits,
@@ -46,13 +48,11 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
 #pragma unroll
     for (int q = 0; q < EPW; ++q) acc[q][t] = 0.0f;
   }
-  // every W_r load of this thread first (H <= 8192: at most 8 float4 a row), then the
-  // activations token by token, each token's loads issued together
-  constexpr int KMAX = 8;
+  // every W_r load of this thread first, then the activations TG tokens at a time
   const int H4 = H >> 2;
-  float4 w[EPW][KMAX];
+  float4 w[EPW][KM];
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) {
+  for (int i = 0; i < KM; ++i) {
     const int h4 = tid + kDecThreads * i;
 #pragma unroll
     for (int q = 0; q < EPW; ++q)
@@ -61,27 +61,35 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
                     : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
-  for (int t = 0; t < kDecMaxT; ++t) {
-    if (t < T) {
-      float4 v[KMAX];
+  for (int t0 = 0; t0 < kDecMaxT; t0 += TG) {
+    if (t0 < T) {
+      float4 v[TG][KM];
 #pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        const int h4 = tid + kDecThreads * i;
-        v[i] = h4 < H4 ? reinterpret_cast<const float4*>(x + (size_t)t * H)[h4]
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int g = 0; g < TG; ++g) {
+        const int t = min(t0 + g, T - 1);          // past T: a valid row, zeroed below
+#pragma unroll
+        for (int i = 0; i < KM; ++i) {
+          const int h4 = tid + kDecThreads * i;
+          v[g][i] = reinterpret_cast<const float4*>(x + (size_t)t * H)[h4 < H4 ? h4 : 0];
+          if (h4 >= H4 || t0 + g >= T) v[g][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        float a = ss[t];
-        a = fmaf(v[i].x, v[i].x, a); a = fmaf(v[i].y, v[i].y, a);
-        a = fmaf(v[i].z, v[i].z, a); a = fmaf(v[i].w, v[i].w, a);
-        ss[t] = a;
+      for (int g = 0; g < TG; ++g) {
+        const int t = t0 + g;
 #pragma unroll
-        for (int q = 0; q < EPW; ++q) {
-          float c = acc[q][t];
-          c = fmaf(w[q][i].x, v[i].x, c); c = fmaf(w[q][i].y, v[i].y, c);
-          c = fmaf(w[q][i].z, v[i].z, c); c = fmaf(w[q][i].w, v[i].w, c);
-          acc[q][t] = c;
+        for (int i = 0; i < KM; ++i) {
+          float a = ss[t];
+          a = fmaf(v[g][i].x, v[g][i].x, a); a = fmaf(v[g][i].y, v[g][i].y, a);
+          a = fmaf(v[g][i].z, v[g][i].z, a); a = fmaf(v[g][i].w, v[g][i].w, a);
+          ss[t] = a;
+#pragma unroll
+          for (int q = 0; q < EPW; ++q) {
+            float c = acc[q][t];
+            c = fmaf(w[q][i].x, v[g][i].x, c); c = fmaf(w[q][i].y, v[g][i].y, c);
+            c = fmaf(w[q][i].z, v[g][i].z, c); c = fmaf(w[q][i].w, v[g][i].w, c);
+            acc[q][t] = c;
+          }
         }
       }
     }
@@ -509,21 +517,50 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
   return false;
 }
 
+// token group: one token at a time when there are few tokens or many W_r registers
+template <int EPW, int KM>
+static void launch_router(int grid, hipStream_t s, const float* x, const float* wr,
+                          const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
+                          float* logits, float* rscale) {
+  constexpr int kTg = EPW * KM >= 16 ? 1 : (EPW * KM >= 8 ? 2 : 4);
+  if (T <= 2 || kTg == 1)
+    hipLaunchKernelGGL((decode_router_kernel<EPW, KM, 1>), dim3(grid), dim3(kDecThreads), 0, s,
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+  else
+    hipLaunchKernelGGL((decode_router_kernel<EPW, KM, kTg>), dim3(grid), dim3(kDecThreads), 0, s,
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+}
+
+template <int EPW>
+static bool dispatch_router(int km, int grid, hipStream_t s, const float* x, const float* wr,
+                            const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
+                            float* logits, float* rscale) {
+  switch (km) {
+    case 1: launch_router<EPW, 1>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+    case 2: launch_router<EPW, 2>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+    case 3: case 4: launch_router<EPW, 4>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+    case 5: case 6: case 7: launch_router<EPW, 7>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+    case 8: launch_router<EPW, 8>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+  }
+  return false;
+}
+
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,
                               float* rscale, hipStream_t s) {
   const int epw = sh.E >= 256 ? 4 : (sh.E >= 128 ? 2 : 1);
   const int use_norm = eps >= 0.0f ? 1 : 0;
   const float e_arg = use_norm ? eps : 0.0f;
+  const int km = (sh.H + 1023) / 1024;
+  const int grid = (sh.E + epw - 1) / epw;
+  bool ok;
   if (epw == 4)
-    hipLaunchKernelGGL(decode_router_kernel<4>, dim3((sh.E + 3) / 4), dim3(kDecThreads), 0, s, x,
-                       wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<4>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
   else if (epw == 2)
-    hipLaunchKernelGGL(decode_router_kernel<2>, dim3((sh.E + 1) / 2), dim3(kDecThreads), 0, s, x,
-                       wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
   else
-    hipLaunchKernelGGL(decode_router_kernel<1>, dim3(sh.E), dim3(kDecThreads), 0, s, x, wr, bias,
-                       T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -229,7 +229,10 @@ static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t st
   const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
   // slots a workgroup takes of one expert; work items: (expert, chunk), at most one partial
   // chunk an expert beyond rows / tch
-  const int tch = (T > 4 && T <= 16) ? 4 : T;
+#ifndef MOE_GEMV_TCH
+#define MOE_GEMV_TCH 4
+#endif
+  const int tch = (T > 4 && T <= 16) ? MOE_GEMV_TCH : T;
   const int rows = T * (sh.k + sh.S);
   grid.y += (rows + tch - 1) / tch;
   hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,
