@@ -37,7 +37,7 @@ template <int EPW, int KM, int TG>
 __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int H, int E, float eps, int use_norm, float* __restrict__ logits,
-    float* __restrict__ rscale) {
+    float* __restrict__ rscale, float* __restrict__ xn) {
   __shared__ float s_red[4][(EPW + 1) * kDecMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * EPW;
@@ -119,7 +119,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
         r = 1.0f / sqrtf(sq / (float)H + eps);
       }
       logits[(size_t)t * E + e] = r * dot + (bias ? bias[e] : 0.0f);
-      if (use_norm && blockIdx.x == 0 && q == 0) rscale[t] = r;
+      if (use_norm && rscale && blockIdx.x == 0 && q == 0) rscale[t] = r;
+    }
+  }
+  // optional normalised rows: workgroup b writes token rows b, b + grid, ... (same r)
+  if (xn && use_norm) {
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+      const int i = EPW * kDecMaxT + t;
+      const float sq = (s_red[0][i] + s_red[1][i]) + (s_red[2][i] + s_red[3][i]);
+      const float r = 1.0f / sqrtf(sq / (float)H + eps);
+      const float4* src = reinterpret_cast<const float4*>(x + (size_t)t * H);
+      float4* dst = reinterpret_cast<float4*>(xn + (size_t)t * H);
+      for (int h4 = tid; h4 < H4; h4 += kDecThreads) {
+        const float4 v = src[h4];
+        dst[h4] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+      }
     }
   }
 }
@@ -521,33 +535,33 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
 template <int EPW, int KM>
 static void launch_router(int grid, hipStream_t s, const float* x, const float* wr,
                           const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
-                          float* logits, float* rscale) {
+                          float* logits, float* rscale, float* xn) {
   constexpr int kTg = EPW * KM >= 16 ? 1 : (EPW * KM >= 8 ? 2 : 4);
   if (T <= 2 || kTg == 1)
     hipLaunchKernelGGL((decode_router_kernel<EPW, KM, 1>), dim3(grid), dim3(kDecThreads), 0, s,
-                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn);
   else
     hipLaunchKernelGGL((decode_router_kernel<EPW, KM, kTg>), dim3(grid), dim3(kDecThreads), 0, s,
-                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale);
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn);
 }
 
 template <int EPW>
 static bool dispatch_router(int km, int grid, hipStream_t s, const float* x, const float* wr,
                             const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
-                            float* logits, float* rscale) {
+                            float* logits, float* rscale, float* xn) {
   switch (km) {
-    case 1: launch_router<EPW, 1>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
-    case 2: launch_router<EPW, 2>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
-    case 3: case 4: launch_router<EPW, 4>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
-    case 5: case 6: case 7: launch_router<EPW, 7>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
-    case 8: launch_router<EPW, 8>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale); return true;
+    case 1: launch_router<EPW, 1>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
+    case 2: launch_router<EPW, 2>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
+    case 3: case 4: launch_router<EPW, 4>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
+    case 5: case 6: case 7: launch_router<EPW, 7>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
+    case 8: launch_router<EPW, 8>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
   }
   return false;
 }
 
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,
-                              float* rscale, hipStream_t s) {
+                              float* rscale, hipStream_t s, float* xn) {
   const int epw = sh.E >= 256 ? 4 : (sh.E >= 128 ? 2 : 1);
   const int use_norm = eps >= 0.0f ? 1 : 0;
   const float e_arg = use_norm ? eps : 0.0f;
@@ -555,11 +569,11 @@ hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
   const int grid = (sh.E + epw - 1) / epw;
   bool ok;
   if (epw == 4)
-    ok = dispatch_router<4>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<4>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
   else if (epw == 2)
-    ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
   else
-    ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale);
+    ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -573,22 +587,17 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   hipError_t err = hipSuccess;
   if (T > kDecodeFusedMaxT) {
     // several tokens: route once (rows normalised into xn), then the slot-chunked GEMVs
-    const float* xin = x;
     if (stages & 1) {
-      if (use_norm) {
-        err = launch_rmsnorm(x, T, sh.H, eps, sc.xn, s);
-        if (err != hipSuccess) return err;
-      }
-      xin = use_norm ? sc.xn : x;
-      err = launch_router_rows(sh, xin, wr, bias, T, -1.0f, sc.logits, nullptr, s);
+      // logits of the normalised rows (r * <x, w_e> + b_e) and the rows themselves, then
+      // top-k and the permutation in one workgroup
+      err = launch_router_rows(sh, x, wr, bias, T, use_norm ? eps : -1.0f, sc.logits, nullptr, s,
+                               use_norm ? sc.xn : nullptr);
       if (err != hipSuccess) return err;
-      err = launch_topk(sh, sc.logits, T, sc.ids, sc.w, s);
-      if (err != hipSuccess) return err;
-      err = launch_permute(sh, sc.ids, sc.w, T, nullptr, nullptr, 0, sc.offsets, sc.sorted_pairs,
-                           sc.pair_slot, sc.count, nullptr, s);
+      err = launch_topk_permute(sh, sc.logits, T, sc.ids, sc.w, sc.offsets, sc.sorted_pairs,
+                                sc.pair_slot, sc.count, s);
       if (err != hipSuccess) return err;
     }
-    xin = use_norm ? sc.xn : x;
+    const float* xin = use_norm ? sc.xn : x;
     if (stages & 2) {
       err = launch_gemv(sh, 0, bank, stride, sc.offsets, sc.sorted_pairs, xin, sc.h, T, s);
       if (err != hipSuccess) return err;

@@ -13,6 +13,7 @@
 // (per-block histograms -> one scan workgroup -> scatter), plus an optional row gather.
 #include "common.h"
 #include "kernels.h"
+#include "route_core.h"
 
 namespace moe {
 
@@ -53,29 +54,18 @@ __device__ __forceinline__ int sanitize_one(int32_t* ids, float* w, int p, int E
   return id;
 }
 
-// Whole permutation in one workgroup: P = T*k <= 1024 pairs and E + S <= 1024 bins.
-__global__ void __launch_bounds__(1024) permute_small_kernel(
-    int32_t* __restrict__ ids, float* __restrict__ w, int T, int k, int E, int S,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ pair_slot, int32_t* __restrict__ invalid_count) {
-  __shared__ int s_id[kSmallThreads];
-  __shared__ int s_cnt[kSmallThreads];
-  __shared__ int s_off[kSmallThreads + 1];
-  __shared__ int s_wave[16];
-  __shared__ int s_bad;
+// Offsets, sorted pairs and the inverse map of P <= 1024 sanitised pair ids in s_id (LDS),
+// by one workgroup of 1024 threads: histogram, scan, stable rank.
+__device__ void permute_small_core(const int* s_id, int P, int T, int E, int S, int* s_cnt,
+                                   int* s_off, int* s_wave, int32_t* __restrict__ offsets,
+                                   int32_t* __restrict__ sorted_pairs,
+                                   int32_t* __restrict__ pair_slot) {
   const int tid = threadIdx.x;
-  const int P = T * k, NB = E + S;
+  const int NB = E + S;
   s_cnt[tid] = 0;
-  if (tid == 0) s_bad = 0;
   __syncthreads();
-  int id = 0;
-  if (tid < P) {
-    int bad = 0;
-    id = sanitize_one(ids, w, tid, E, bad);
-    if (bad) atomicAdd(&s_bad, 1);          // a count: the order of adds does not matter
-    s_id[tid] = id;
-    atomicAdd(&s_cnt[id], 1);
-  }
+  const int id = tid < P ? s_id[tid] : 0;
+  if (tid < P) atomicAdd(&s_cnt[id], 1);
   __syncthreads();
   const int c = tid < E ? s_cnt[tid] : (tid < NB ? T : 0);
   const int incl = block_scan_1024(c, s_wave);
@@ -92,7 +82,60 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(
     sorted_pairs[slot] = tid;
     pair_slot[tid] = slot;
   }
+}
+
+// Whole permutation in one workgroup: P = T*k <= 1024 pairs and E + S <= 1024 bins.
+__global__ void __launch_bounds__(1024) permute_small_kernel(
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int k, int E, int S,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_slot, int32_t* __restrict__ invalid_count) {
+  __shared__ int s_id[kSmallThreads];
+  __shared__ int s_cnt[kSmallThreads];
+  __shared__ int s_off[kSmallThreads + 1];
+  __shared__ int s_wave[16];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int P = T * k;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < P) {
+    int bad = 0;
+    s_id[tid] = sanitize_one(ids, w, tid, E, bad);
+    if (bad) atomicAdd(&s_bad, 1);          // a count: the order of adds does not matter
+  }
+  __syncthreads();
+  permute_small_core(s_id, P, T, E, S, s_cnt, s_off, s_wave, offsets, sorted_pairs, pair_slot);
   if (tid == 0) *invalid_count = s_bad;
+}
+
+// Decode batches: top-k of T logit rows (one wave a row, from LDS) and the permutation of the
+// route table they make, in one workgroup.  Top-k ids are in range, so nothing is sanitised.
+__global__ void __launch_bounds__(1024) topk_permute_kernel(
+    const float* __restrict__ logits, int T, int k, int E, int S, int gating, int renorm,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ invalid_count) {
+  extern __shared__ float s_l[];             // T x E logits
+  __shared__ int s_id[kSmallThreads];
+  __shared__ float s_w[kSmallThreads];
+  __shared__ int s_cnt[kSmallThreads];
+  __shared__ int s_off[kSmallThreads + 1];
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = T * k;
+  for (int t = wave; t < T; t += kSmallThreads / 64) {
+    for (int e = lane; e < E; e += 64) s_l[t * E + e] = logits[(size_t)t * E + e];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+    wave_topk(s_l + t * E, E, k, gating, renorm, s_id + t * k, s_w + t * k);
+  }
+  __syncthreads();
+  if (tid < P) {
+    ids[tid] = s_id[tid];
+    w[tid] = s_w[tid];
+  }
+  permute_small_core(s_id, P, T, E, S, s_cnt, s_off, s_wave, offsets, sorted_pairs, pair_slot);
+  if (tid == 0) *invalid_count = 0;
 }
 
 // Pass 1: sanitise, per-block histogram -> counts[blk * E + e]; invalid count per block.
@@ -229,6 +272,23 @@ hipError_t launch_permute(const Shape& sh, int32_t* ids, float* w, int T, const 
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_kernel, dim3(rows, (sh.H / 4 + 255) / 256), dim3(256), 0, s, x,
                      sorted_pairs, T, sh.k, sh.H, x_perm_bf16, x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_permute(const Shape& sh, const float* logits, int T, int32_t* ids,
+                               float* w, int32_t* offsets, int32_t* sorted_pairs,
+                               int32_t* pair_slot, int32_t* invalid_count, hipStream_t s) {
+  const size_t lds = (size_t)T * sh.E * sizeof(float);
+  if (T == 0) return hipSuccess;
+  if (!use_small(sh, T) || lds > 32 * 1024) {
+    hipError_t e = launch_topk(sh, logits, T, ids, w, s);
+    if (e != hipSuccess) return e;
+    return launch_permute(sh, ids, w, T, nullptr, nullptr, 0, offsets, sorted_pairs, pair_slot,
+                          invalid_count, nullptr, s);
+  }
+  hipLaunchKernelGGL(topk_permute_kernel, dim3(1), dim3(kSmallThreads), lds, s, logits, T, sh.k,
+                     sh.E, sh.S, sh.gating, sh.renorm, ids, w, offsets, sorted_pairs, pair_slot,
+                     invalid_count);
   return hipGetLastError();
 }
 
