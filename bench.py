@@ -258,7 +258,7 @@ def _oracle_expert(args):
                               for w in ("gate", "up", "down")])
 
 
-def cpu_baseline(n_layers, T):
+def cpu_baseline(n_layers, T, min_seconds=10.0):
     """The oracle (fp64 numpy) decoding T tokens through the first n_layers layers; inputs are
     prepared first (host generator + oracle quantiser, in worker processes), then the oracle's
     chain is timed with its BLAS limited to one thread."""
@@ -290,19 +290,25 @@ def cpu_baseline(n_layers, T):
             banks.append(bank)
             routers.append(wr)
     t_prep = time.time() - t_prep
-    x = G.activations(wl, T).astype(np.float64)
+    # whole passes over the prepared layers until at least min_seconds of oracle work
+    passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for l in range(n_layers):
-            xn = omoe.rmsnorm(x)
-            x = x + omoe.moe_layer(xn, routers[l], None, banks[l], stride, desc)
-        dt = time.perf_counter() - t0
-    per_layer = dt / n_layers
+        while True:
+            x = G.activations(wl, T).astype(np.float64)
+            for l in range(n_layers):
+                xn = omoe.rmsnorm(x)
+                x = x + omoe.moe_layer(xn, routers[l], None, banks[l], stride, desc)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds or passes >= 50:
+                break
+    per_layer = dt / (n_layers * passes)
     return dict(value=T / (per_layer * wl.layers), unit="tok/s", cores=1, kind="oracle",
                 sample=f"{T} token(s) through layers 0..{n_layers - 1} of the {wl.layers}-layer "
-                       f"decode stack (fp64 numpy oracle incl. dequantisation of the routed "
-                       f"experts; BLAS 1 thread), {dt:.2f} s timed, scaled to {wl.layers} "
-                       f"layers; input prep {t_prep:.1f} s untimed",
+                       f"decode stack, {passes} passes (fp64 numpy oracle incl. dequantisation of "
+                       f"the routed experts; BLAS 1 thread), {dt:.2f} s timed, scaled to "
+                       f"{wl.layers} layers; input prep {t_prep:.1f} s untimed",
                 seconds=dt)
 
 
@@ -318,7 +324,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--cpu-layers", type=int, default=12)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (the reference kernel "
                          "of known traffic for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -355,7 +362,7 @@ def main():
             f"down {p['dn_ms']:.3f} ms)")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_layers, d["T"])
+        cpu = cpu_baseline(args.cpu_layers, d["T"], args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
     rec = {
