@@ -72,9 +72,9 @@ def decode_bench(args):
     import torch
     import quantized_moe_expert_amd as M
     from quantized_moe_expert_amd import layer as L
-    from synth.configs import XING4_DECODE
+    from synth.configs import WORKLOADS
 
-    wl = XING4_DECODE
+    wl = WORKLOADS[args.decode_workload]
     s = wl.shape
     T = args.tokens
     eps = 1e-6
@@ -195,7 +195,8 @@ def decode_bench(args):
         gemv_gbs=gemv_gbs, expert_bytes_step=expert_bytes_step, chain_us=chain_us,
         router_bytes_step=router_bytes_step,
         floor_us=(expert_bytes_step + router_bytes_step) / (HBM_PEAK_GBS * 1e9) * 1e6,
-        layers=wl.layers, keep=keep)
+        layers=wl.layers, keep=keep, name=wl.name, H=s.hidden, F=s.ffn, E=s.n_experts,
+        k=s.top_k, gating="sigmoid" if s.gating == M.MOE_GATING_SIGMOID else "softmax")
 
 
 def prefill_bench(args):
@@ -239,7 +240,13 @@ def prefill_bench(args):
     flop_dn = 2.0 * rows * s.ffn * s.hidden
     off = buf.offsets.cpu()
     counts = (off[1:] - off[:-1])[:s.n_experts]
+    # algorithmic bytes of the two GEMMs: weights of the experts with rows (once each),
+    # x_perm (bf16) in, h (bf16) out and in, o (fp32) out
+    used = int(((off[1:] - off[:-1]) > 0).sum().item())
+    gemm_bytes = (used * s.expert_bytes + rows * s.hidden * 2 + 2 * rows * s.ffn * 2
+                  + rows * s.hidden * 4)
     return dict(workload=wl.name, T=T, layer_ms=layer_ms, gu_ms=gu_ms, dn_ms=dn_ms,
+                gemm_gbs=gemm_bytes / ((gu_ms + dn_ms) * 1e-3) / 1e9, gemm_bytes=gemm_bytes,
                 gemm_tflops=(flop_gu + flop_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12,
                 gu_tflops=flop_gu / (gu_ms * 1e-3) / 1e12,
                 dn_tflops=flop_dn / (dn_ms * 1e-3) / 1e12,
@@ -317,7 +324,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--tokens", type=int, default=1, help="decode batch (1 or 16)")
+    ap.add_argument("--tokens", type=int, default=1, help="decode batch (1 to 16)")
+    ap.add_argument("--decode-workload", default="xing4_decode",
+                    help="decode stack: xing4_decode (headline), qwen3next_like, dsv41_like")
     ap.add_argument("--event-reps", type=int, default=20,
                     help="back-to-back launches a layer timed for the dominant kernel")
     ap.add_argument("--prefill-workload", default="xing4_prefill")
@@ -361,7 +370,7 @@ def main():
             f"grouped GEMM {p['gemm_tflops']:.1f} TFLOP/s (gate/up {p['gu_ms']:.3f} ms, "
             f"down {p['dn_ms']:.3f} ms)")
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.decode_workload == "xing4_decode":
         cpu = cpu_baseline(args.cpu_layers, d["T"], args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
@@ -379,20 +388,25 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"xing4_decode: {d['T']} token(s) x {d['layers']} chained MoE layers, "
-                        f"H 3584, 64 experts top-4 sigmoid + 1 shared, F 1024, IQ4_NL",
+            "workload": f"{d['name']}: {d['T']} token(s) x {d['layers']} chained MoE layers, "
+                        f"H {d['H']}, {d['E']} experts top-{d['k']} {d['gating']} + 1 shared, "
+                        f"F {d['F']}, IQ4_NL",
             "global_batch": d["T"], "layers": d["layers"], "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": "decode_gateup_kernel (routing + IQ4_NL dequant-GEMV gate/up + SwiGLU)",
+            "kernel": ("decode_gateup_kernel (routing + IQ4_NL dequant-GEMV gate/up + SwiGLU)"
+                       if d["T"] <= 4 else
+                       "gemv_kernel<..., true> (IQ4_NL dequant-GEMV gate/up + SwiGLU)"),
             "bytes_note": "active experts' gate+up IQ4_NL bytes + activations in + h out",
             "bound": "hbm",
             "achieved": round(d["gu_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(d["gu_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic("decode_gateup_kernel"),
+            "traffic": (traffic("decode_gateup_kernel")
+                        if d["T"] == 1 and d["name"] == "xing4_decode" else None),
             "traffic_note": "HBM bytes a launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from "
-                            "profiles/pmc_traffic_xing4.txt; null if the kernel changed since",
+                            "profiles/pmc_traffic_xing4.txt (1-token xing4 decode); null if the "
+                            "kernel changed since or for another workload",
             "bytes_per_launch": round(d["gu_avg_bytes"]),
             "avg_launch_us": round(d["gu_avg_us"], 3),
         },
@@ -418,8 +432,12 @@ def main():
             "layer_tok_s": round(p["T"] / (p["layer_ms"] * 1e-3), 1),
             "flop_per_layer": p["flop"],
             "expert_load_max_over_mean": round(p["load_max_over_mean"], 2),
-            "gate_up_traffic_bytes": traffic("gemm_kernel<true>"),
-            "down_traffic_bytes": traffic("gemm_kernel<false>"),
+            "gemm_GBps": round(p["gemm_gbs"], 1),
+            "gemm_frac_of_hbm": round(p["gemm_gbs"] / HBM_PEAK_GBS, 4),
+            "gate_up_traffic_bytes": (traffic("gemm_kernel<true>")
+                                      if p["workload"] == "xing4_prefill" else None),
+            "down_traffic_bytes": (traffic("gemm_kernel<false>")
+                                   if p["workload"] == "xing4_prefill" else None),
         }
     if cpu:
         rec["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}

@@ -562,7 +562,8 @@ static bool dispatch_router(int km, int grid, hipStream_t s, const float* x, con
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,
                               float* rscale, hipStream_t s, float* xn) {
-  const int epw = sh.E >= 256 ? 4 : (sh.E >= 128 ? 2 : 1);
+  // experts a workgroup: at least 256 workgroups where the expert count allows
+  const int epw = sh.E >= 256 ? 1 : (sh.E >= 128 ? 2 : 1);
   const int use_norm = eps >= 0.0f ? 1 : 0;
   const float e_arg = use_norm ? eps : 0.0f;
   const int km = (sh.H + 1023) / 1024;
@@ -622,7 +623,10 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   const bool wide = T > 1 && nb == 112;
   const DecGeom gu = wide ? DecGeom{16, 7} : dec_geom(nb);
   if (gu.lpr == 0) return hipErrorInvalidValue;
-  const int passes = wide ? 2 : 4;
+  // several tokens over many experts make the in-workgroup routing costly: fewer, larger
+  // workgroups (8 passes)
+  const bool heavy = !wide && T > 1 && sh.E >= 256;
+  const int passes = wide ? 2 : (heavy ? 8 : 4);
   const int orows_wg = (kDecThreads / 64) * passes * (64 / gu.lpr) / 2;
   const int max_active = (int)std::min<int64_t>(sh.E, (int64_t)T * sh.k) + sh.S;
   const int tch = T;                               // every token of an expert in one workgroup
@@ -633,7 +637,13 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
     launch_up<16, 7, 2, 2>(grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
                            sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h, tch);
     ok = true;
-  } else if (T > 1 && gu.bpl <= 2)
+  } else if (heavy && gu.bpl <= 2)
+    ok = dispatch_up<2, 8>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
+  else if (heavy)
+    ok = dispatch_up<1, 8>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
+                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
+  else if (T > 1 && gu.bpl <= 2)
     ok = dispatch_up<2, 4>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
                            sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
   else
