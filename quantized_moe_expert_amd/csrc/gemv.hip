@@ -61,14 +61,115 @@ __device__ void find_work(const int32_t* __restrict__ offsets, int n_bins, int i
   chunk_out = 0;
 }
 
-template <int LPR, int BPL, int MT, bool GATEUP>
-__global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
-    const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, const float* __restrict__ in,
-    float* __restrict__ out, int H, int F, int E, int S, int k, int T, int tch) {
+// The work of one (expert, slot chunk) item, MTR tokens a tile.
+template <int LPR, int BPL, int MTR, bool GATEUP>
+__device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_t row_bytes,
+                                         int NB, int NOUT, int K, int F, int H, int T, int k,
+                                         int P, int slot0, int m,
+                                         const int32_t* __restrict__ sorted_pairs,
+                                         const float* __restrict__ in, float* __restrict__ out,
+                                         uint32_t* s_x, const uint32_t* s_tab, int* s_row) {
   constexpr int RPP = 64 / LPR;               // rows per pass per wave
   constexpr int WROWS = kPasses * RPP;        // weight rows per wave
   constexpr int OROWS = GATEUP ? WROWS / 2 : WROWS;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane / LPR, lig = lane % LPR;
+  const bool odd = (lig & 1) != 0;                   // block parity == lane parity
+  const int orow0 = (blockIdx.x * (kGemvThreads / 64) + wave) * OROWS;
+
+  // token rows of the first tile (needs sorted_pairs: one dependent L2 round trip)
+  if (tid < MTR && tid < m) {
+    const int sl = slot0 + tid;
+    s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+  }
+  lds_barrier();
+
+  // 1) activation loads of the first tile, then every weight load of this wave (loads
+  //    complete in issue order: the activations arrive first); the weight rows stay in
+  //    registers for all token tiles
+  Stager<4 * MTR> stg;
+  // (addresses formed from the kernel argument keep the global address space: global loads,
+  //  counted on vmcnt only)
+  stg.load(NB, LPR * BPL, min(MTR, m), MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
+           [&](int) { return 1.0f; });
+  RawBlock raw[kPasses][BPL];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int i = p * RPP + g;
+    int r, wr;
+    if (GATEUP) {
+      r = orow0 + (i < OROWS ? i : i - OROWS);
+      wr = (i < OROWS ? 0 : F) + r;
+    } else {
+      r = orow0 + i;
+      wr = r;
+    }
+    const bool ok = r < NOUT;
+    const uint8_t* rowp = mat + (int64_t)(ok ? wr : 0) * row_bytes;
+    // unconditional loads (a lane past the row end reads a block of the same parity inside
+    // it; its activations are zero padding): a static load count, no divergent branches
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+      const int kb = lig + LPR * b;
+      raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
+    }
+  }
+
+  // 2)-3) per token tile: activations -> LDS (once per workgroup), dequantise and dot.  The
+  // first tile is peeled so that its staging waits only on its own (earlier) loads.
+  auto tile = [&](int t0, int n_tok) {
+    // 3) dequantise and dot
+    float acc[kPasses][MTR];
+    rows_dot<kPasses, LPR, BPL, MTR>(raw, odd, s_tab, s_x, lig, acc);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+      for (int u = 0; u < MTR; ++u) acc[p][u] = group_sum_dpp<LPR>(acc[p][u]);
+    if (lig != 0) return;
+#pragma unroll
+    for (int u = 0; u < MTR; ++u) {
+      if (u >= n_tok) continue;
+      const int64_t s = slot0 + t0 + u;
+      if (GATEUP) {
+#pragma unroll
+        for (int p = 0; p < kPasses / 2; ++p) {
+          const int r = orow0 + p * RPP + g;
+          if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + kPasses / 2][u];
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < kPasses; ++p) {
+          const int r = orow0 + p * RPP + g;
+          if (r < H) out[s * H + r] = acc[p][u];
+        }
+      }
+    }
+  };
+  stg.store(s_x);
+  lds_barrier();
+  tile(0, min(MTR, m));
+  for (int t0 = MTR; t0 < m; t0 += MTR) {
+    const int n_tok = min(MTR, m - t0);
+    lds_barrier();
+    if (tid < n_tok) {
+      const int sl = slot0 + t0 + tid;
+      s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+    }
+    lds_barrier();
+    stg.load(NB, LPR * BPL, n_tok, MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
+             [&](int) { return 1.0f; });
+    stg.store(s_x);
+    lds_barrier();
+    tile(t0, n_tok);
+  }
+}
+
+template <int LPR, int BPL, int MT, bool GATEUP>
+__global__ void __launch_bounds__(kGemvThreads, BPL <= 3 ? 2 : 1) gemv_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, const float* __restrict__ in,
+    float* __restrict__ out, int H, int F, int E, int S, int k, int T, int tch) {
   extern __shared__ uint32_t s_x[];           // MT tokens x LPR*BPL blocks x kXStride dwords
   __shared__ uint32_t s_tab[256];
   __shared__ int s_expert, s_chunk;
@@ -105,96 +206,13 @@ __global__ void __launch_bounds__(kGemvThreads) gemv_kernel(
   const int m = min(tch, m_all - tb);
   const int P = T * k;
 
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane / LPR, lig = lane % LPR;
-  const bool odd = (lig & 1) != 0;                   // block parity == lane parity
-  const int orow0 = (blockIdx.x * (kGemvThreads / 64) + wave) * OROWS;
-
-  // token rows of the first tile (needs sorted_pairs: one dependent L2 round trip)
-  if (tid < MT && tid < m) {
-    const int sl = slot0 + tid;
-    s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
-  }
-  lds_barrier();
-
-  // 1) activation loads of the first tile, then every weight load of this wave (loads
-  //    complete in issue order: the activations arrive first); the weight rows stay in
-  //    registers for all token tiles
-  Stager<4 * MT> stg;
-  // (addresses formed from the kernel argument keep the global address space: global loads,
-  //  counted on vmcnt only)
-  stg.load(NB, LPR * BPL, min(MT, m), MT, [&](int u) { return in + (int64_t)s_row[u] * K; },
-           [&](int) { return 1.0f; });
-  RawBlock raw[kPasses][BPL];
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int i = p * RPP + g;
-    int r, wr;
-    if (GATEUP) {
-      r = orow0 + (i < OROWS ? i : i - OROWS);
-      wr = (i < OROWS ? 0 : F) + r;
-    } else {
-      r = orow0 + i;
-      wr = r;
-    }
-    const bool ok = r < NOUT;
-    const uint8_t* rowp = mat + (int64_t)(ok ? wr : 0) * row_bytes;
-    // unconditional loads (a lane past the row end reads a block of the same parity inside
-    // it; its activations are zero padding): a static load count, no divergent branches
-#pragma unroll
-    for (int b = 0; b < BPL; ++b) {
-      const int kb = lig + LPR * b;
-      raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
-    }
-  }
-
-  // 2)-3) per token tile: activations -> LDS (once per workgroup), dequantise and dot.  The
-  // first tile is peeled so that its staging waits only on its own (earlier) loads.
-  auto tile = [&](int t0, int n_tok) {
-    // 3) dequantise and dot
-    float acc[kPasses][MT];
-    rows_dot<kPasses, LPR, BPL, MT>(raw, odd, s_tab, s_x, lig, acc);
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-#pragma unroll
-      for (int u = 0; u < MT; ++u) acc[p][u] = group_sum_dpp<LPR>(acc[p][u]);
-    if (lig != 0) return;
-#pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      if (u >= n_tok) continue;
-      const int64_t s = slot0 + t0 + u;
-      if (GATEUP) {
-#pragma unroll
-        for (int p = 0; p < kPasses / 2; ++p) {
-          const int r = orow0 + p * RPP + g;
-          if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + kPasses / 2][u];
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
-          const int r = orow0 + p * RPP + g;
-          if (r < H) out[s * H + r] = acc[p][u];
-        }
-      }
-    }
-  };
-  stg.store(s_x);
-  lds_barrier();
-  tile(0, min(MT, m));
-  for (int t0 = MT; t0 < m; t0 += MT) {
-    const int n_tok = min(MT, m - t0);
-    lds_barrier();
-    if (tid < n_tok) {
-      const int sl = slot0 + t0 + tid;
-      s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
-    }
-    lds_barrier();
-    stg.load(NB, LPR * BPL, n_tok, MT, [&](int u) { return in + (int64_t)s_row[u] * K; },
-             [&](int) { return 1.0f; });
-    stg.store(s_x);
-    lds_barrier();
-    tile(t0, n_tok);
-  }
+  // a chunk holding one token runs the one-token tiles (half the dot products of a tile of 2)
+  if (MT > 1 && m == 1)
+    gemv_run<LPR, BPL, 1, GATEUP>(mat, row_bytes, NB, NOUT, K, F, H, T, k, P, slot0, m,
+                                  sorted_pairs, in, out, s_x, s_tab, s_row);
+  else
+    gemv_run<LPR, BPL, MT, GATEUP>(mat, row_bytes, NB, NOUT, K, F, H, T, k, P, slot0, m,
+                                   sorted_pairs, in, out, s_x, s_tab, s_row);
 }
 
 // ---- host-side dispatch ----------------------------------------------------------------
