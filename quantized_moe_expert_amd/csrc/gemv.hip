@@ -31,6 +31,9 @@ constexpr int kGemvThreads = 256;
 #define MOE_GEMV_PASSES 8
 #endif
 constexpr int kPasses = MOE_GEMV_PASSES;   // weight rows a lane group visits (even)
+// rows a lane group visits at BPL blocks a lane: half as many for the longest rows, which
+// keeps the weight registers of a wave (PASSES x BPL blocks) within two waves a SIMD
+constexpr int passes_for(int bpl) { return bpl >= 4 ? kPasses / 2 : kPasses; }
 
 // Work item `item` of the list of (expert, chunk of tch slots) pairs over the experts with
 // slots, in index order: e (-1 past the end) and the chunk index.  One wave.
@@ -69,8 +72,9 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
                                          const int32_t* __restrict__ sorted_pairs,
                                          const float* __restrict__ in, float* __restrict__ out,
                                          uint32_t* s_x, const uint32_t* s_tab, int* s_row) {
+  constexpr int NPASS = passes_for(BPL);
   constexpr int RPP = 64 / LPR;               // rows per pass per wave
-  constexpr int WROWS = kPasses * RPP;        // weight rows per wave
+  constexpr int WROWS = NPASS * RPP;        // weight rows per wave
   constexpr int OROWS = GATEUP ? WROWS / 2 : WROWS;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -93,9 +97,9 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
   //  counted on vmcnt only)
   stg.load(NB, LPR * BPL, min(MTR, m), MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
            [&](int) { return 1.0f; });
-  RawBlock raw[kPasses][BPL];
+  RawBlock raw[NPASS][BPL];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
+  for (int p = 0; p < NPASS; ++p) {
     const int i = p * RPP + g;
     int r, wr;
     if (GATEUP) {
@@ -120,10 +124,10 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
   // first tile is peeled so that its staging waits only on its own (earlier) loads.
   auto tile = [&](int t0, int n_tok) {
     // 3) dequantise and dot
-    float acc[kPasses][MTR];
-    rows_dot<kPasses, LPR, BPL, MTR>(raw, odd, s_tab, s_x, lig, acc);
+    float acc[NPASS][MTR];
+    rows_dot<NPASS, LPR, BPL, MTR>(raw, odd, s_tab, s_x, lig, acc);
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p)
+    for (int p = 0; p < NPASS; ++p)
 #pragma unroll
       for (int u = 0; u < MTR; ++u) acc[p][u] = group_sum_dpp<LPR>(acc[p][u]);
     if (lig != 0) return;
@@ -133,13 +137,13 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
       const int64_t s = slot0 + t0 + u;
       if (GATEUP) {
 #pragma unroll
-        for (int p = 0; p < kPasses / 2; ++p) {
+        for (int p = 0; p < NPASS / 2; ++p) {
           const int r = orow0 + p * RPP + g;
-          if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + kPasses / 2][u];
+          if (r < F) out[s * F + r] = silu(acc[p][u]) * acc[p + NPASS / 2][u];
         }
       } else {
 #pragma unroll
-        for (int p = 0; p < kPasses; ++p) {
+        for (int p = 0; p < NPASS; ++p) {
           const int r = orow0 + p * RPP + g;
           if (r < H) out[s * H + r] = acc[p][u];
         }
@@ -166,7 +170,7 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
 }
 
 template <int LPR, int BPL, int MT, bool GATEUP>
-__global__ void __launch_bounds__(kGemvThreads, BPL <= 3 ? 2 : 1) gemv_kernel(
+__global__ void __launch_bounds__(kGemvThreads, 2) gemv_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ in,
     float* __restrict__ out, int H, int F, int E, int S, int k, int T, int tch) {
@@ -294,7 +298,8 @@ hipError_t launch_gemv(const Shape& sh, int stage, const uint8_t* bank, int64_t 
   const GemvGeom gm = pick_geom(K / 32);
   if (gm.lpr == 0) return hipErrorInvalidValue;
   const int rpp = 64 / gm.lpr;
-  const int orows_wave = gu ? kPasses * rpp / 2 : kPasses * rpp;
+  const int np = passes_for(gm.bpl);
+  const int orows_wave = gu ? np * rpp / 2 : np * rpp;
   const int orows_wg = orows_wave * (kGemvThreads / 64);
   const int max_active = (int)std::min<int64_t>((int64_t)sh.E, (int64_t)T * sh.k) + sh.S;
   dim3 grid((NOUT + orows_wg - 1) / orows_wg, max_active);
