@@ -521,10 +521,11 @@ static void launch_down(hipStream_t s, const uint8_t* bank, int64_t stride, cons
 static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_t stride,
                           const float* h, const int32_t* off, const int32_t* ps, const float* w,
                           int T, const Shape& sh, const float* residual, float* y) {
-  // rows per workgroup 4 * NRP * RPP: about 16 for every group width
+  // rows per workgroup 4 * NRP * RPP: about 16 for every group width, 8 for one-block rows of
+  // 32 lanes (FFN 1024: twice the workgroups, 448 over 256 CUs, measured faster)
 #define DN(L, B, N) \
   if (gm.lpr == L && gm.bpl == B) { launch_down<L, B, N>(s, bank, stride, h, off, ps, w, T, sh, residual, y); return true; }
-  DN(64, 1, 4) DN(64, 2, 4) DN(64, 3, 4) DN(64, 4, 4) DN(32, 1, 2) DN(32, 2, 2) DN(32, 3, 2)
+  DN(64, 1, 4) DN(64, 2, 4) DN(64, 3, 4) DN(64, 4, 4) DN(32, 1, 1) DN(32, 2, 2) DN(32, 3, 2)
   DN(32, 4, 2) DN(16, 1, 1) DN(16, 2, 1) DN(16, 3, 1) DN(16, 4, 1) DN(8, 1, 1) DN(8, 2, 1)
   DN(4, 1, 1) DN(4, 2, 1)
 #undef DN
