@@ -166,42 +166,56 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   const int P = T * k, NBIN = E + S;
   const int nch = (T + tch - 1) / tch;             // token chunks an expert is split into
   s_tab[tid] = pair_table_entry(tid);
-  for (int i = tid; i < NBIN; i += kDecThreads) s_cnt[i] = 0;
-  for (int t = wave; t < T; t += 4)
-    wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
-  __syncthreads();
-  for (int p = tid; p < P; p += kDecThreads) atomicAdd(&s_cnt[s_ids[p]], 1);   // counts only
-  if (tid < S) s_cnt[E + tid] = T;
-  __syncthreads();
+  // the first nch rows of the grid take the shared expert: slots P.., tokens 0..T-1 in
+  // order, known without the routing, so their weight stream starts at once (and they are
+  // dispatched first); the routed experts take the rows from y0 on
+  const int y0 = S > 0 ? nch : 0;
+  const bool shared_wg = (int)blockIdx.y < y0;
+  if (shared_wg) {
+    if (tid == 0) {
+      s_e = E;
+      s_slot0 = P;
+      s_m = T;
+    }
+    __syncthreads();
+  } else {
+    for (int i = tid; i < NBIN; i += kDecThreads) s_cnt[i] = 0;
+    for (int t = wave; t < T; t += 4)
+      wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
+    __syncthreads();
+    for (int p = tid; p < P; p += kDecThreads) atomicAdd(&s_cnt[s_ids[p]], 1);   // counts only
+    if (tid < S) s_cnt[E + tid] = T;
+    __syncthreads();
 
-  // the blockIdx.y-th expert with routes, and the number of slots before it
-  if (wave == 0) {
-    const int target = blockIdx.y / nch;
-    int seen = 0, run = 0, found = -1, slot0 = 0;
-    for (int base = 0; base < NBIN && found < 0; base += 64) {
-      const int b = base + lane;
-      const int c = b < NBIN ? s_cnt[b] : 0;
-      const uint64_t mask = __ballot(c > 0);
-      const int cnt = __popcll(mask);
-      if (target < seen + cnt) {
-        uint64_t mm = mask;
-        for (int i = 0; i < target - seen; ++i) mm &= mm - 1;
-        const int pos = __ffsll((long long)mm) - 1;
-        // slot counts are small integers: exact as float sums
-        slot0 = run + (int)group_sum_dpp<64>((float)(lane < pos ? c : 0));
-        found = base + pos;
-      } else {
-        seen += cnt;
-        run += (int)group_sum_dpp<64>((float)c);
+    // the blockIdx.y-th routed expert with routes, and the number of slots before it
+    if (wave == 0) {
+      const int target = ((int)blockIdx.y - y0) / nch;
+      int seen = 0, run = 0, found = -1, slot0 = 0;
+      for (int base = 0; base < E && found < 0; base += 64) {
+        const int b = base + lane;
+        const int c = b < E ? s_cnt[b] : 0;
+        const uint64_t mask = __ballot(c > 0);
+        const int cnt = __popcll(mask);
+        if (target < seen + cnt) {
+          uint64_t mm = mask;
+          for (int i = 0; i < target - seen; ++i) mm &= mm - 1;
+          const int pos = __ffsll((long long)mm) - 1;
+          // slot counts are small integers: exact as float sums
+          slot0 = run + (int)group_sum_dpp<64>((float)(lane < pos ? c : 0));
+          found = base + pos;
+        } else {
+          seen += cnt;
+          run += (int)group_sum_dpp<64>((float)c);
+        }
+      }
+      if (lane == 0) {
+        s_e = found;
+        s_slot0 = slot0;
+        s_m = found >= 0 ? s_cnt[found] : 0;
       }
     }
-    if (lane == 0) {
-      s_e = found;
-      s_slot0 = slot0;
-      s_m = found >= 0 ? s_cnt[found] : 0;
-    }
+    __syncthreads();
   }
-  __syncthreads();
   const int e = s_e;
   if (e < 0) return;
   const int slot0 = s_slot0;
@@ -255,8 +269,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
     }
   }
 
-  // workgroup (0, 0) publishes the route table and the permutation
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  // workgroup (0, y0), the first routed one, publishes the route table and the permutation
+  if (blockIdx.x == 0 && (int)blockIdx.y == y0) {
     int loc[4], run = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
