@@ -364,28 +364,15 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   uint32_t* s_x = s_dyn;                                   // rows_total x NBP x kXStride
   float* s_o = reinterpret_cast<float*>(s_dyn + rows_total * NBP * kXStride);  // R x rows
 
-  // every slot's h: loads first (no dependency; they arrive before the weight stream)
+  // load order: the route table (the routed weight addresses wait on it), every slot's h,
+  // then the shared expert's weights, which need no route table (loads complete in order)
+  int ov[(1025 + kDecThreads - 1) / kDecThreads];
+#pragma unroll
+  for (int j = 0; j < (1025 + kDecThreads - 1) / kDecThreads; ++j)
+    ov[j] = offsets[min(tid + kDecThreads * j, NBIN)];
   Stager<UPT> stg;
   stg.load(NB, NBP, rows_total, rows_total,
            [&](int u) -> const float* { return h + (int64_t)u * F; }, [&](int) { return 1.0f; });
-  s_tab[tid] = pair_table_entry(tid);
-  for (int i = tid; i <= NBIN; i += kDecThreads) s_off[i] = offsets[i];
-  lds_barrier();
-  // compact list of experts with slots (index order)
-  if (wave == 0) {
-    int seen = 0;
-    for (int base = 0; base < NBIN; base += 64) {
-      const int b = base + lane;
-      const bool ne = b < NBIN && s_off[b + 1] > s_off[b];
-      const uint64_t mask = __ballot(ne);
-      if (ne) s_act[seen + __popcll(mask & ((1ull << lane) - 1))] = b;
-      seen += __popcll(mask);
-    }
-    if (lane == 0) s_nact = seen;
-  }
-  lds_barrier();
-  const int nact = s_nact;
-  const int npass = nact * NRP;
 
   const int g = lane / LPR, lig = lane % LPR;
   const bool odd = (lig & 1) != 0;
@@ -393,8 +380,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   const int64_t row_bytes = (int64_t)NB * kBlockBytes;
   const int64_t down_off = 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
 
-  auto load_pass = [&](int p, RawBlock (&dst)[BPL]) {
-    const int e = s_act[p / NRP];
+  auto load_rows = [&](int e, int p, RawBlock (&dst)[BPL]) {
     const int r = r0 + wave * RW + (p % NRP) * RPP + g;
     const bool ok = r < H;
     const uint8_t* rowp = bank + (int64_t)e * stride + down_off + (int64_t)(ok ? r : 0) * row_bytes;
@@ -404,11 +390,41 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
       dst[b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
     }
   };
-
+  // pass p: expert s_act[p / NRP], row pass p % NRP; the shared expert's passes come first
+  auto load_pass = [&](int p, RawBlock (&dst)[BPL]) { load_rows(s_act[p / NRP], p, dst); };
+  const int pre = S > 0 ? NRP : 0;
   RawBlock ring[kDownRing][BPL];
 #pragma unroll
   for (int d = 0; d < kDownRing; ++d)
-    if (d < npass) load_pass(d, ring[d]);
+    if (d < pre) load_rows(E, d, ring[d]);
+
+  s_tab[tid] = pair_table_entry(tid);
+#pragma unroll
+  for (int j = 0; j < (1025 + kDecThreads - 1) / kDecThreads; ++j)
+    if (tid + kDecThreads * j <= NBIN) s_off[tid + kDecThreads * j] = ov[j];
+  lds_barrier();
+  // compact list of experts with slots: the shared expert, then the routed ones in index order
+  if (wave == 0) {
+    int seen = 0;
+    if (S > 0) {
+      if (lane == 0) s_act[0] = E;
+      seen = 1;
+    }
+    for (int base = 0; base < E; base += 64) {
+      const int b = base + lane;
+      const bool ne = b < E && s_off[b + 1] > s_off[b];
+      const uint64_t mask = __ballot(ne);
+      if (ne) s_act[seen + __popcll(mask & ((1ull << lane) - 1))] = b;
+      seen += __popcll(mask);
+    }
+    if (lane == 0) s_nact = seen;
+  }
+  lds_barrier();
+  const int nact = s_nact;
+  const int npass = nact * NRP;
+#pragma unroll
+  for (int d = 0; d < kDownRing; ++d)
+    if (d >= pre && d < npass) load_pass(d, ring[d]);
 
   // every slot's h -> LDS as bf16 (hi, lo) pairs
   stg.store(s_x);
