@@ -91,7 +91,10 @@ def test_prefill_layer_full_size(name, T, n_check):
 
 @pytest.mark.parametrize("name,T,n_check", [("tiny", 4, 4), ("xing4_decode", 1, 1),
                                             ("xing4_decode", 16, 2), ("qwen3next_like", 1, 1),
-                                            ("qwen3next_like", 2, 2), ("dsv41_like", 16, 1)])
+                                            ("qwen3next_like", 2, 2), ("dsv41_like", 16, 1),
+                                            # ragged batches: partial token tiles and chunks
+                                            ("xing4_decode", 3, 3), ("xing4_decode", 7, 2),
+                                            ("qwen3next_like", 5, 2), ("dsv41_like", 9, 1)])
 def test_fused_decode_layer_full_size(name, T, n_check):
     wl = WORKLOADS[name]
     s = wl.shape
