@@ -89,6 +89,18 @@ _SIGNATURES = {
 }
 
 _lib = None
+_DEFAULT_LIB = LIB_PATH
+
+
+def _check_fresh(path):
+    """Refuse a library built from other sources than the ones in the tree (a stale build)."""
+    from . import build as _build
+    rec = path + ".digest"
+    want = _build.source_digest(path)
+    have = open(rec).read().strip() if os.path.exists(rec) else None
+    if have != want:
+        raise ImportError(f"{path} was built from other sources than the tree holds (stale "
+                          "build): rebuild it with `python -m quantized_moe_expert_amd.build`")
 
 
 def lib():
@@ -98,6 +110,8 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m quantized_moe_expert_amd.build`")
+        if LIB_PATH == _DEFAULT_LIB:
+            _check_fresh(LIB_PATH)
         l = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(l, name)

@@ -4,6 +4,7 @@ Every source is compiled to an object in parallel, then linked.  All HIP code is
 with packed-fp32 instruction selection disabled.
 """
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -25,6 +26,20 @@ LIBS = {
     os.path.join(ROOT, "synth", "libmoe_synth.so"): [
         os.path.join(ROOT, "synth", "csrc", "synth.hip")],
 }
+
+
+def source_digest(lib):
+    """sha256 of the sources a library is built from (its .hip files and every header beside
+    them), in a fixed order; written next to the library so a stale build can be refused."""
+    srcs = LIBS[lib]
+    dirs = sorted({os.path.dirname(s) for s in srcs})
+    headers = [os.path.join(d, f) for d in dirs for f in sorted(os.listdir(d)) if f.endswith(".h")]
+    h = hashlib.sha256()
+    for f in list(srcs) + headers:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def _compile(src, obj, verbose):
@@ -62,6 +77,8 @@ def build(verbose: bool = False, jobs: int = None) -> list:
         if r.returncode != 0:
             raise RuntimeError(f"link failed for {lib}:\n{r.stderr}")
         os.replace(tmp, lib)
+        with open(lib + ".digest", "w") as fh:
+            fh.write(source_digest(lib) + "\n")
         built.append(lib)
         if verbose:
             print("built", lib, flush=True)

@@ -600,9 +600,7 @@ hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
   const int km = (sh.H + 1023) / 1024;
   const int grid = (sh.E + epw - 1) / epw;
   bool ok;
-  if (epw == 4)
-    ok = dispatch_router<4>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
-  else if (epw == 2)
+  if (epw == 2)
     ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
   else
     ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);

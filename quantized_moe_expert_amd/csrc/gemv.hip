@@ -27,10 +27,8 @@
 namespace moe {
 
 constexpr int kGemvThreads = 256;
-#ifndef MOE_GEMV_PASSES
-#define MOE_GEMV_PASSES 8
-#endif
-constexpr int kPasses = MOE_GEMV_PASSES;   // weight rows a lane group visits (even)
+constexpr int kPasses = 8;                 // weight rows a lane group visits (even)
+constexpr int kBatchChunk = 4;             // slots a workgroup takes of an expert, 4 < T <= 16
 // rows a lane group visits at BPL blocks a lane: half as many for the longest rows, which
 // keeps the weight registers of a wave (PASSES x BPL blocks) within two waves a SIMD
 constexpr int passes_for(int bpl) { return bpl >= 4 ? kPasses / 2 : kPasses; }
@@ -251,10 +249,7 @@ static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t st
   const size_t lds = (size_t)MT * LPR * BPL * kXStride * 4;
   // slots a workgroup takes of one expert; work items: (expert, chunk), at most one partial
   // chunk an expert beyond rows / tch
-#ifndef MOE_GEMV_TCH
-#define MOE_GEMV_TCH 4
-#endif
-  const int tch = (T > 4 && T <= 16) ? MOE_GEMV_TCH : T;
+  const int tch = (T > 4 && T <= 16) ? kBatchChunk : T;
   const int rows = T * (sh.k + sh.S);
   grid.y += (rows + tch - 1) / tch;
   hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,

@@ -76,3 +76,11 @@ def test_decode_chain_checks_before_enqueueing():
     with pytest.raises(M.MoeError) as ei:
         M.moe_decode_chain(d, arr, 1, None, 1, 1e-6, None, None, None, 0, stream=0)
     assert ei.value.status == M.MOE_ERR_NULL
+
+
+def test_stale_library_is_refused(monkeypatch):
+    from quantized_moe_expert_amd import build as B
+    M._check_fresh(M.LIB_PATH)                    # the tree's build matches its sources
+    monkeypatch.setattr(B, "source_digest", lambda lib: "0" * 64)
+    with pytest.raises(ImportError, match="stale"):
+        M._check_fresh(M.LIB_PATH)
