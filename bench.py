@@ -439,6 +439,10 @@ def main():
             "down_traffic_bytes": (traffic("gemm_kernel<false>")
                                    if p["workload"] == "xing4_prefill" else None),
         }
+    dig = M.LIB_PATH + ".digest"
+    rec["build"] = {"lib": os.path.basename(M.LIB_PATH),
+                    "sources_sha256": open(dig).read().strip()[:16] if os.path.exists(dig) else None,
+                    "device": torch.cuda.get_device_name(0)}
     if cpu:
         rec["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
         rec["cpu_baseline"]["value"] = round(cpu["value"], 4)
