@@ -171,11 +171,27 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   // dispatched first); the routed experts take the rows from y0 on
   const int y0 = S > 0 ? nch : 0;
   const bool shared_wg = (int)blockIdx.y < y0;
+  const bool publisher = blockIdx.x == 0 && (int)blockIdx.y == y0;
+  const bool fast1 = T == 1 && !publisher;
   if (shared_wg) {
     if (tid == 0) {
       s_e = E;
       s_slot0 = P;
       s_m = T;
+    }
+    __syncthreads();
+  } else if (fast1) {
+    // one token: a routed workgroup needs only which expert is the target-th member of the
+    // top-k set in index order (its slot is that rank); order and weights are the
+    // publisher's business (it runs the full top-k below)
+    if (wave == 0) {
+      const int target = (int)blockIdx.y - y0;
+      const int e1 = wave_topk_member_any(logits, E, k, target);
+      if (lane == 0) {
+        s_e = e1;
+        s_slot0 = target;
+        s_m = e1 >= 0 ? 1 : 0;
+      }
     }
     __syncthreads();
   } else {
@@ -226,7 +242,9 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
 
   // tokens of expert e, in pair order
   if (wave == 0) {
-    if (e < E) {
+    if (fast1) {
+      if (lane == 0) s_tok[0] = 0;
+    } else if (e < E) {
       int seen = 0;
       for (int base = 0; base < P; base += 64) {
         const int p = base + lane;
@@ -270,7 +288,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   }
 
   // workgroup (0, y0), the first routed one, publishes the route table and the permutation
-  if (blockIdx.x == 0 && (int)blockIdx.y == y0) {
+  if (publisher) {
     int loc[4], run = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -82,6 +82,64 @@ __device__ __forceinline__ int wave_select(const float* __restrict__ l, int E, i
   return my_e;
 }
 
+// The target-th member, in expert-index order, of the top-k set of one token's logits (the
+// set wave_select picks: the k largest keys, ties to the lower index), or -1 past the set;
+// wave-uniform.  No order or weights: the k-th largest key is found bit by bit from the top
+// (32 rounds of a compare and a ballot count), which is far shorter than k rounds of
+// wave-wide arg-max when only membership is needed.
+template <int KPL>
+__device__ __forceinline__ int wave_topk_member(const float* __restrict__ l, int E, int k,
+                                                int target) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? order_bits(l[e]) + 1u : 0u;
+  }
+  // tau = the largest value with at least k keys >= tau: the k-th largest key
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  int need = k;                                   // members equal to tau, lowest index first
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) need -= __popcll(__ballot(key[i] > tau));
+  int seen = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    uint64_t eq = __ballot(key[i] == tau && tau != 0u);
+    uint64_t take = 0;
+    while (need > 0 && eq) {
+      const uint64_t low = eq & (~eq + 1);
+      take |= low;
+      eq ^= low;
+      --need;
+    }
+    uint64_t sel = __ballot(key[i] > tau) | take;
+    const int c = __popcll(sel);
+    if (target < seen + c) {
+      for (int j = 0; j < target - seen; ++j) sel &= sel - 1;
+      return __ffsll((long long)sel) - 1 + 64 * i;
+    }
+    seen += c;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int wave_topk_member_any(const float* __restrict__ l, int E, int k,
+                                                    int target) {
+  if (E <= 64) return wave_topk_member<1>(l, E, k, target);
+  if (E <= 128) return wave_topk_member<2>(l, E, k, target);
+  if (E <= 256) return wave_topk_member<4>(l, E, k, target);
+  if (E <= 512) return wave_topk_member<8>(l, E, k, target);
+  return wave_topk_member<16>(l, E, k, target);
+}
+
 // ids[0..k-1], w[0..k-1] of one token's logits l[0..E-1] (E <= 1024, k <= 32); all 64
 // lanes of the wave take part; lanes j < k write entry j.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int k, int gating,
