@@ -228,3 +228,32 @@ def test_invalid_routes_contribute_nothing():
     bank_np, stride = oracle_bank(wl, 0, range(s.n_experts + 1))
     ref = omoe.moe_layer(xh, None, None, bank_np, stride, desc_of(s), ids=ids, weights=w)
     assert_close(buf.y.cpu().numpy(), ref, REL_L2_GEMV, "invalid routes")
+
+
+@pytest.mark.parametrize("name,lift", [("xing4_decode", (20, 40)), ("qwen3next_like", (3, 500, 77)),
+                                       ("tiny", (5,))])
+def test_one_token_decode_with_exact_logit_ties(name, lift):
+    """Every expert gets the same router row, so all logits tie except the lifted experts'
+    (bias +1): the top-k set is the lifted experts plus the lowest-index tied ones.  The
+    routed workgroups of the one-token path pick their experts by set membership, the
+    publishing one by the full top-k; both must agree with the oracle's tie rule."""
+    wl = WORKLOADS[name]
+    s = wl.shape
+    T = 1
+    wr_h = np.repeat(G.router_weight(wl, 0)[:1], s.n_experts, axis=0)
+    bias_h = np.zeros(s.n_experts, np.float32)
+    for e in lift:
+        bias_h[e] = 1.0
+    wr = torch.from_numpy(wr_h).to(DEV)
+    bias = torch.from_numpy(bias_h).to(DEV)
+    bank_t, bank = L.make_bank(wl, 0)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(s, T)
+    y = L.decode_layer_fused(buf, x, wr, bias, bank).clone()
+    torch.cuda.synchronize()
+    xh = G.activations(wl, T)
+    ref, parts = oracle_layer(wl, 0, xh, return_parts=True, bias=bias_h, w_router=wr_h)
+    want = sorted(lift) + [e for e in range(s.n_experts) if e not in lift][:s.top_k - len(lift)]
+    assert sorted(parts["ids"][0].tolist()) == sorted(want)
+    assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
+    assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"ties {name}")
