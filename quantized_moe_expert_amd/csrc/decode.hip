@@ -41,6 +41,16 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
   __shared__ float s_red[4][(EPW + 1) * kDecMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * EPW;
+  // grid row y takes tokens [y * tpg, y * tpg + tpg): fewer activation rows a workgroup reads
+  {
+    const int tpg = (T + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int t0 = (int)blockIdx.y * tpg;
+    T = min(tpg, T - t0);
+    x += (size_t)t0 * H;
+    logits += (size_t)t0 * E;
+    if (rscale) rscale += t0;
+    if (xn) xn += (size_t)t0 * H;
+  }
   float acc[EPW][kDecMaxT], ss[kDecMaxT];
 #pragma unroll
   for (int t = 0; t < kDecMaxT; ++t) {
@@ -582,11 +592,12 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
 
 // token group: one token at a time when there are few tokens or many W_r registers
 template <int EPW, int KM>
-static void launch_router(int grid, hipStream_t s, const float* x, const float* wr,
+static void launch_router(dim3 grid, hipStream_t s, const float* x, const float* wr,
                           const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
                           float* logits, float* rscale, float* xn) {
   constexpr int kTg = EPW * KM >= 16 ? 1 : (EPW * KM >= 8 ? 2 : 4);
-  if (T <= 2 || kTg == 1)
+  const int tpg = (T + (int)grid.y - 1) / (int)grid.y;
+  if (tpg <= 2 || kTg == 1)
     hipLaunchKernelGGL((decode_router_kernel<EPW, KM, 1>), dim3(grid), dim3(kDecThreads), 0, s,
                        x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn);
   else
@@ -595,7 +606,7 @@ static void launch_router(int grid, hipStream_t s, const float* x, const float* 
 }
 
 template <int EPW>
-static bool dispatch_router(int km, int grid, hipStream_t s, const float* x, const float* wr,
+static bool dispatch_router(int km, dim3 grid, hipStream_t s, const float* x, const float* wr,
                             const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
                             float* logits, float* rscale, float* xn) {
   switch (km) {
@@ -616,7 +627,8 @@ hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
   const int use_norm = eps >= 0.0f ? 1 : 0;
   const float e_arg = use_norm ? eps : 0.0f;
   const int km = (sh.H + 1023) / 1024;
-  const int grid = (sh.E + epw - 1) / epw;
+  // more than 4 tokens: groups of at most 4 tokens along the grid's y
+  const dim3 grid((sh.E + epw - 1) / epw, T > 4 ? (T + 3) / 4 : 1);
   bool ok;
   if (epw == 2)
     ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
