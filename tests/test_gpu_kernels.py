@@ -161,10 +161,30 @@ def test_route_exact_ties_and_nan():
                 assert list(ids[t]).index(a) < list(ids[t]).index(bb)
 
 
+@pytest.mark.parametrize("E,k,gating,renorm,T", [(1023, 32, 0, 1, 5), (1023, 32, 1, 0, 3),
+                                                 (1000, 17, 1, 1, 20), (33, 32, 0, 1, 2)])
+def test_route_largest_expert_counts_and_k(E, k, gating, renorm, T):
+    """Top-k at the descriptor's limits (E + S = 1024 bins, k = 32; k = E - 1) on synthetic
+    logits: the selection equals a full stable sort of the GPU's own logits, the weights the
+    closed forms of the oracle."""
+    H = 256
+    rng = np.random.default_rng(E + k + T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    wr[7] = wr[3]                                  # an exact tie
+    desc = M.make_desc(H, 128, E, k, 1, gating, renorm, T)
+    ids, w, lg = _route_gpu(desc, x, wr, None, T, k, E)
+    assert np.array_equal(ids, omoe.select_topk(lg.astype(np.float64), k))
+    ref_w = omoe.gating_weights(lg.astype(np.float64), ids, gating, renorm)
+    assert np.allclose(w, ref_w, rtol=2e-5, atol=1e-6)
+
+
 # ---- permutation ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,k,E", [(0, 4, 64), (1, 4, 64), (16, 4, 64), (4, 2, 8), (37, 10, 512),
-                                   (2048, 4, 64), (8192, 6, 384), (1000, 3, 1023), (300, 1, 5)])
+                                   (2048, 4, 64), (8192, 6, 384), (1000, 3, 1023), (300, 1, 5),
+                                   # the one-workgroup path's limit (T k = 1024) and one past it
+                                   (256, 4, 64), (257, 4, 64), (32, 32, 1023)])
 def test_permute_bitexact(T, k, E):
     rng = np.random.default_rng(T * 7 + k + E)
     ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
