@@ -162,16 +162,18 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
     gload(0);
     for (int kt = 0; kt < NKT; ++kt) {
       lds_barrier();     // every wave is done reading the previous step's tiles
-      // A -> LDS in pair order: dword j = (a[j], a[j+16]); rows past the expert's end are 0
+      // A -> LDS in pair order: dword j = (a[j], a[j+16]).  Rows past the expert's end are not
+      // written: they only feed output rows that are never stored
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (!aok[i]) continue;
         const uint32_t a0[4] = {ga[i][0].x, ga[i][0].y, ga[i][0].z, ga[i][0].w};
         const uint32_t a1[4] = {ga[i][1].x, ga[i][1].y, ga[i][1].z, ga[i][1].w};
         uint32_t d[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          d[2 * w] = aok[i] ? __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u) : 0u;
-          d[2 * w + 1] = aok[i] ? __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u) : 0u;
+          d[2 * w] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+          d[2 * w + 1] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
         }
         uint4* dst = reinterpret_cast<uint4*>(&sA[ar[i] * kLdsStride + ak[i] * 16 + 8 * ac[i]]);
         dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
@@ -200,6 +202,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
       }
       if (kt + 1 < NKT) gload(kt + 1);
       lds_barrier();
+      // a wave whose 64 slot rows are all past the tile's end has nothing to compute
+      if (wm * 64 < rows_valid)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         bf16x8_t af[4], bfr[4];
