@@ -16,6 +16,8 @@
 //
 // The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 128) over the
 // experts); a persistent grid walks it, so nothing depends on host-known expert loads.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -139,6 +141,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
       arow[i] = in + (int64_t)(slot0 + m0 + (aok[i] ? ar[i] : 0)) * K;
     }
 
+    // 16-row groups of this wave's 64 rows that hold slot rows of the tile
+    const int wgroups = min(4, max(0, (rows_valid - wm * 64 + 15) >> 4));
     f32x4_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -202,24 +206,35 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
       }
       if (kt + 1 < NKT) gload(kt + 1);
       lds_barrier();
-      // a wave whose 64 slot rows are all past the tile's end has nothing to compute
-      if (wm * 64 < rows_valid)
+      // only the 16-row groups of this wave that hold slot rows of the tile are multiplied
+      // (a wave whose 64 rows are all past the tile's end has nothing to compute)
+      auto mma = [&](auto gc) __attribute__((always_inline)) {
+        constexpr int G = decltype(gc)::value;
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        bf16x8_t af[4], bfr[4];
+        for (int kb = 0; kb < kKB; ++kb) {
+          bf16x8_t af[G], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(
-              &sA[(wm * 64 + 16 * i + c16) * kLdsStride + kb * 16 + 4 * q]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-              &sB[(wn * 64 + 16 * j + c16) * kLdsStride + kb * 16 + 4 * q]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < G; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t*>(
+                &sA[(wm * 64 + 16 * i + c16) * kLdsStride + kb * 16 + 4 * q]);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+                &sB[(wn * 64 + 16 * j + c16) * kLdsStride + kb * 16 + 4 * q]);
+#pragma unroll
+          for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+      };
+      switch (wgroups) {
+        case 0: break;
+        case 1: mma(std::integral_constant<int, 1>{}); break;
+        case 2: mma(std::integral_constant<int, 2>{}); break;
+        case 3: mma(std::integral_constant<int, 3>{}); break;
+        default: mma(std::integral_constant<int, 4>{}); break;
       }
     }
 
