@@ -156,9 +156,12 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
     auto gload = [&](int kt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // (lanes of rows past the tile's end load nothing: their values are never staged)
         const uint16_t* src = arow[i] + (kt * kKB + ak[i]) * 32 + 8 * ac[i];
-        ga[i][0] = *reinterpret_cast<const uint4*>(src);
-        ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
+        if (aok[i]) {
+          ga[i][0] = *reinterpret_cast<const uint4*>(src);
+          ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) gb[i] = load_block(brow[i], kt * kKB + bk[i]);
