@@ -7,12 +7,12 @@
 //
 // Tiles: 128 slot rows x 128 weight rows per workgroup (4 waves, 2 x 2, 64 x 64 each), K in
 // steps of 4 IQ4_NL blocks.  Weight tiles are dequantised once per workgroup into LDS as
-// bf16(d * c[q]) (fp32 product, exact; one RNE rounding); activation tiles are staged through
-// LDS.  Inside every 32-wide block both operands use the same K order -- pair j holds
-// elements (j, j+16) -- which is the order of the code bytes, so a code byte dequantises to
-// one packed bf16 pair.  For GATE_UP the workgroup's 128 weight rows are 64 gate rows and the
-// 64 matching up rows, arranged so that a lane holds g and u of the same output and applies
-// SwiGLU in registers.
+// bf16(d * c[q]) (fp32 product, exact; one RNE rounding); activation tiles are copied into
+// LDS as they are, in natural K order, with coalesced 16-byte loads.  A code byte holds
+// elements j and j+16 of its block, so the dequantisation pairs the lookups of two adjacent
+// code bytes: their low nibbles give elements (2m, 2m+1), their high nibbles (16+2m, 17+2m).
+// For GATE_UP the workgroup's 128 weight rows are 64 gate rows and the 64 matching up rows,
+// arranged so that a lane holds g and u of the same output and applies SwiGLU in registers.
 //
 // The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 128) over the
 // experts); a persistent grid walks it, so nothing depends on host-known expert loads.
@@ -32,6 +32,7 @@ constexpr int kXcds = 8;               // XCDs of an MI355X (each with its own L
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool GATEUP>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
@@ -127,18 +128,17 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
       }
       brow[i] = wmat + (int64_t)wr * row_bytes;
     }
-    // activation rows this thread stages (4 units: row, block, half)
-    const uint16_t* arow[4];
-    int ar[4], ak[4], ac[4];
-    bool aok[4];
+    // activation chunks this thread stages (8 units of 16 B: row u >> 4, chunk u & 15).  Rows
+    // past the tile's end copy row 0 instead (their output rows are never stored): unconditional
+    // loads keep the compiler's load counting exact, so the loads stay in flight
+    const uint16_t* arow[8];
+    int aoff[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int u = tid + kGemmThreads * i;
-      ar[i] = u >> 3;
-      ak[i] = (u >> 1) & 3;
-      ac[i] = u & 1;
-      aok[i] = ar[i] < rows_valid;
-      arow[i] = in + (int64_t)(slot0 + m0 + (aok[i] ? ar[i] : 0)) * K;
+      const int r = u >> 4, c = u & 15;
+      arow[i] = in + (int64_t)(slot0 + m0 + (r < rows_valid ? r : 0)) * K + 8 * c;
+      aoff[i] = r * kLdsStride + 4 * c;
     }
 
     // 16-row groups of this wave's 64 rows that hold slot rows of the tile
@@ -149,44 +149,30 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // K loop, software-pipelined: the global loads of step kt+1 are in flight while the
-    // MFMAs of step kt run; barriers order LDS only, so they do not wait for those loads.
-    uint4 ga[4][2];
+    // K loop, software-pipelined: the global loads of step kt+1 are issued as soon as the
+    // registers of step kt are in LDS (activations first, then weights) and stay in flight
+    // while the MFMAs of step kt run; barriers order LDS only.
+    u32x4_t ga[4][2];   // (a native vector type: whole-struct copies would go through scratch)
     RawBlock gb[2];
-    auto gload = [&](int kt) {
+    auto gload_a = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // (lanes of rows past the tile's end load nothing: their values are never staged)
-        const uint16_t* src = arow[i] + (kt * kKB + ak[i]) * 32 + 8 * ac[i];
-        if (aok[i]) {
-          ga[i][0] = *reinterpret_cast<const uint4*>(src);
-          ga[i][1] = *reinterpret_cast<const uint4*>(src + 16);
-        }
-      }
+      for (int i = 0; i < 8; ++i)
+        ga[i >> 1][i & 1] = *reinterpret_cast<const u32x4_t*>(arow[i] + kt * kKB * 32);
+    };
+    auto gload_b = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) gb[i] = load_block(brow[i], kt * kKB + bk[i]);
     };
-    gload(0);
+    gload_a(0);
+    gload_b(0);
     for (int kt = 0; kt < NKT; ++kt) {
       lds_barrier();     // every wave is done reading the previous step's tiles
-      // A -> LDS in pair order: dword j = (a[j], a[j+16]).  Rows past the expert's end are not
-      // written: they only feed output rows that are never stored
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!aok[i]) continue;
-        const uint32_t a0[4] = {ga[i][0].x, ga[i][0].y, ga[i][0].z, ga[i][0].w};
-        const uint32_t a1[4] = {ga[i][1].x, ga[i][1].y, ga[i][1].z, ga[i][1].w};
-        uint32_t d[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          d[2 * w] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
-          d[2 * w + 1] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&sA[ar[i] * kLdsStride + ak[i] * 16 + 8 * ac[i]]);
-        dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
-        dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
-      }
-      // B -> LDS: dequantise to bf16(d * c) pairs
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4_t*>(&sA[aoff[i]]) = ga[i >> 1][i & 1];
+      if (kt + 1 < NKT) gload_a(kt + 1);
+      // B -> LDS: dequantise to bf16(d * c) in natural K order: dword m < 8 holds elements
+      // (2m, 2m+1), the low nibbles of code bytes 2m and 2m+1; dword 8+m their high nibbles
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const bool odd = (bk[i] & 1) != 0;
@@ -195,20 +181,23 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
         block_codes(gb[i], odd, cw);
         uint32_t o[16];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const float2 t = s_tab[(cw[cc] >> (8 * y)) & 0xFFu];
-            o[4 * cc + y] = pack_bf16x2(t.x * dsc, t.y * dsc);
-          }
+        for (int m = 0; m < 8; ++m) {
+          const float2 ta = s_tab[(cw[m >> 1] >> (16 * (m & 1))) & 0xFFu];
+          const float2 tb = s_tab[(cw[m >> 1] >> (16 * (m & 1) + 8)) & 0xFFu];
+          o[m] = pack_bf16x2(ta.x * dsc, tb.x * dsc);
+          o[8 + m] = pack_bf16x2(ta.y * dsc, tb.y * dsc);
+        }
         uint4* dst = reinterpret_cast<uint4*>(&sB[bn[i] * kLdsStride + bk[i] * 16]);
         dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
         dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
         dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
         dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
       }
-      if (kt + 1 < NKT) gload(kt + 1);
+      if (kt + 1 < NKT) gload_b(kt + 1);
       lds_barrier();
+      // the MFMA phase runs at raised wave priority, so that on a SIMD shared with a wave of
+      // the other workgroup the matrix core is fed first and the staging fills the gaps
+      __builtin_amdgcn_s_setprio(1);
       // only the 16-row groups of this wave that hold slot rows of the tile are multiplied
       // (a wave whose 64 rows are all past the tile's end has nothing to compute)
       auto mma = [&](auto gc) __attribute__((always_inline)) {
@@ -239,6 +228,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
         case 3: mma(std::integral_constant<int, 3>{}); break;
         default: mma(std::integral_constant<int, 4>{}); break;
       }
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // epilogue: lane holds column c16 of each 16x16 sub-tile, rows 4q .. 4q+3

@@ -290,6 +290,56 @@ def test_gemv_against_oracle(name, T, stage):
         assert_close(got[a:b][:, sample], ref, REL_L2_GEMV, f"{name} e={e} {stage}")
 
 
+# expert row counts on every edge of the GEMM's 128-row tiles and 16-row MFMA groups
+_EDGE_COUNTS = {3: 1, 10: 15, 17: 16, 22: 17, 29: 63, 33: 64, 40: 65, 45: 127, 51: 128,
+                58: 129, 61: 256, 63: 300}
+
+
+@pytest.mark.parametrize("stage", ["gate_up", "down"])
+def test_grouped_gemm_tile_edges(stage):
+    """Slot ranges of 0, 1, 15, 16, 17, 63 .. 65, 127 .. 129, 256 and 300 rows (empty first
+    and last bins, a shared bin of 47): every row of every non-empty expert against the oracle
+    on sampled columns, and nothing written past the last slot."""
+    wl = WORKLOADS["xing4_prefill"]
+    s = wl.shape
+    rng = np.random.default_rng(zlib.crc32(f"gemm-edges/{stage}".encode()))
+    counts = np.zeros(s.n_experts + 1, np.int64)
+    for e, c in _EDGE_COUNTS.items():
+        counts[e] = c
+    counts[s.n_experts] = 47
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n_rows = int(off[-1])
+    T = -(-n_rows // (s.top_k + 1))
+    rows = T * (s.top_k + 1)
+    used = [e for e in range(s.n_experts + 1) if counts[e] > 0]
+    bank_t, bank = L.make_bank(wl, 0, experts=used)
+    desc = L.desc_of(s, T)
+    K, nout = (s.hidden, s.ffn) if stage == "gate_up" else (s.ffn, s.hidden)
+    xin = (rng.standard_normal((rows, K)) * (1.0 if stage == "gate_up" else 0.7)).astype(np.float32)
+    dt = torch.bfloat16 if stage == "gate_up" else torch.float32
+    out = torch.full((rows, nout), np.nan, dtype=dt, device=DEV)
+    M.moe_grouped_gemm_iq4nl(desc, M.MOE_STAGE_GATE_UP if stage == "gate_up" else M.MOE_STAGE_DOWN,
+                             bank, _to_dev(off), _bf16_tensor(xin), out, T)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isnan(got[n_rows:]).all(), "rows past the last slot were written"
+    sample = _sample_rows(nout, 48, rng)
+    for e in used:
+        a, b = int(off[e]), int(off[e + 1])
+        xs = xin[a:b].astype(np.float64)
+        if stage == "gate_up":
+            wg = _oracle_rows(wl, e, "gate", sample)
+            wu = _oracle_rows(wl, e, "up", sample)
+            ref = omoe.expert_gate_up(wg, wu, xs)
+            bound = gate_up_bf16_bound(wg, wu, xs)
+        else:
+            wd = _oracle_rows(wl, e, "down", sample)
+            ref = omoe.expert_down(wd, xs)
+            bound = down_bf16_bound(wd, xin[a:b])
+        assert_within_bound(got[a:b][:, sample], ref, bound, REL_L2_MFMA,
+                            f"edges e={e} rows={b - a} {stage}")
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("xing4_prefill", 300), ("qwen3next_like", 200),
                                     ("dsv41_like", 260)])
 @pytest.mark.parametrize("stage", ["gate_up", "down"])
