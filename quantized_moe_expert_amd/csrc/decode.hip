@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   constexpr int RPP = 64 / LPR;
   constexpr int WROWS = kUpPasses * RPP;
   constexpr int OROWS = WROWS / 2;
-  extern __shared__ uint32_t s_x[];
+  extern __shared__ __align__(16) uint32_t s_x[];
   __shared__ uint32_t s_tab[256];
   __shared__ int s_ids[kDecMaxT * kDecMaxK];
   __shared__ float s_w[kDecMaxT * kDecMaxK];
@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   constexpr int RPP = 64 / LPR;
   constexpr int RW = NRP * RPP;                  // rows per wave
   constexpr int R = 4 * RW;                      // rows per workgroup
-  extern __shared__ uint32_t s_dyn[];
+  extern __shared__ __align__(16) uint32_t s_dyn[];
   __shared__ uint32_t s_tab[256];
   __shared__ int s_off[1025];
   __shared__ int s_act[1024];

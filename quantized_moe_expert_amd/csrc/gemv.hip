@@ -20,6 +20,8 @@
 // multiplies the pair with the activation pair (x_j, x_{j+16}) twice, once for the hi and once
 // for the lo bf16 part of x.  The block sum is scaled by its fp16 d in fp32 and accumulated
 // in fp32.  Row sums are reduced across the LPR lanes by a fixed butterfly.
+#include <algorithm>
+
 #include "common.h"
 #include "gemv_core.h"
 #include "kernels.h"
@@ -34,29 +36,43 @@ constexpr int kBatchChunk = 4;             // slots a workgroup takes of an expe
 constexpr int passes_for(int bpl) { return bpl >= 4 ? kPasses / 2 : kPasses; }
 
 // Work item `item` of the list of (expert, chunk of tch slots) pairs over the experts with
-// slots, in index order: e (-1 past the end) and the chunk index.  One wave.
+// slots, in index order: e (-1 past the end) and the chunk index.  One wave.  The offsets are
+// read 256 bins at a time (four unconditional loads a lane, one memory round trip), not one
+// dependent round trip per 64 bins.
 __device__ void find_work(const int32_t* __restrict__ offsets, int n_bins, int item, int tch,
                           int& e_out, int& chunk_out) {
   const int lane = threadIdx.x & 63;
   int before = 0;
-  for (int base = 0; base < n_bins; base += 64) {
-    const int b = base + lane;
-    const int c = b < n_bins ? (offsets[b + 1] - offsets[b] + tch - 1) / tch : 0;
-    int incl = c;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
+  for (int base = 0; base < n_bins; base += 256) {
+    int cnt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = base + 64 * j + lane;
+      const int bb = min(b, n_bins - 1);
+      const int m = offsets[bb + 1] - offsets[bb];
+      // (masked, not selected: a select makes the compiler branch around the division and
+      //  the load, one round trip each)
+      cnt[j] = ((m + tch - 1) / tch) & -(int)(b < n_bins);
     }
-    const int total = __shfl(incl, 63, 64);
-    if (item < before + total) {
-      const int lo = before + incl - c;
-      const uint64_t mask = __ballot(item >= lo && item < lo + c);
-      const int hl = __ffsll((long long)mask) - 1;
-      e_out = base + hl;
-      chunk_out = item - __shfl(lo, hl, 64);
-      return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = cnt[j];
+      int incl = c;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (item < before + total) {
+        const int lo = before + incl - c;
+        const uint64_t mask = __ballot(item >= lo && item < lo + c);
+        const int hl = __ffsll((long long)mask) - 1;
+        e_out = base + 64 * j + hl;
+        chunk_out = item - __shfl(lo, hl, 64);
+        return;
+      }
+      before += total;
     }
-    before += total;
   }
   e_out = -1;
   chunk_out = 0;
@@ -80,21 +96,22 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
   const bool odd = (lig & 1) != 0;                   // block parity == lane parity
   const int orow0 = (blockIdx.x * (kGemvThreads / 64) + wave) * OROWS;
 
-  // token rows of the first tile (needs sorted_pairs: one dependent L2 round trip)
-  if (tid < MTR && tid < m) {
-    const int sl = slot0 + tid;
-    s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
-  }
-  lds_barrier();
-
-  // 1) activation loads of the first tile, then every weight load of this wave (loads
-  //    complete in issue order: the activations arrive first); the weight rows stay in
-  //    registers for all token tiles
-  Stager<4 * MTR> stg;
-  // (addresses formed from the kernel argument keep the global address space: global loads,
-  //  counted on vmcnt only)
-  stg.load(NB, LPR * BPL, min(MTR, m), MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
-           [&](int) { return 1.0f; });
+  // 1) the token rows of the first tile (a read of sorted_pairs), then every weight load of
+  //    this wave, then, once the token rows are known, the activations.  The weight addresses
+  //    do not depend on the token rows, so the weights stream during that round trip; loads
+  //    complete in issue order, so the activations arrive right behind the weights.  The
+  //    weight rows stay in registers for all token tiles
+  // the token rows of the first two tiles are read at once (the second tile then needs no
+  // read of sorted_pairs of its own)
+  constexpr int PRE = 2 * MTR;
+  const int sl0 = slot0 + min(tid, PRE - 1);
+  // (unconditional, clamped to a routed slot, and a relaxed atomic read so that the compiler
+  //  keeps it ahead of the weight loads instead of sinking it to its use)
+  const int pair0 =
+      GATEUP ? __hip_atomic_load(sorted_pairs + min(sl0, P - 1), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP)
+             : 0;
+  __builtin_amdgcn_sched_barrier(0);   // ... issued ahead of the weight loads
   RawBlock raw[NPASS][BPL];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
@@ -117,6 +134,15 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
       raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // the token rows are used only after every weight load
+  if (tid < PRE && tid < m)
+    s_row[tid] = GATEUP ? (sl0 < P ? pair0 / k : (sl0 - P) % T) : sl0;
+  lds_barrier();
+  Stager<4 * MTR> stg;
+  // (addresses formed from the kernel argument keep the global address space: global loads,
+  //  counted on vmcnt only)
+  stg.load(NB, LPR * BPL, min(MTR, m), MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
+           [&](int) { return 1.0f; });
 
   // 2)-3) per token tile: activations -> LDS (once per workgroup), dequantise and dot.  The
   // first tile is peeled so that its staging waits only on its own (earlier) loads.
@@ -154,12 +180,16 @@ __device__ __forceinline__ void gemv_run(const uint8_t* __restrict__ mat, int64_
   for (int t0 = MTR; t0 < m; t0 += MTR) {
     const int n_tok = min(MTR, m - t0);
     lds_barrier();
-    if (tid < n_tok) {
-      const int sl = slot0 + t0 + tid;
-      s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+    int rb = t0;                      // the tile's token rows start at s_row[rb]
+    if (t0 >= PRE) {
+      if (tid < n_tok) {
+        const int sl = slot0 + t0 + tid;
+        s_row[tid] = GATEUP ? (sl < P ? sorted_pairs[sl] / k : (sl - P) % T) : sl;
+      }
+      lds_barrier();
+      rb = 0;
     }
-    lds_barrier();
-    stg.load(NB, LPR * BPL, n_tok, MTR, [&](int u) { return in + (int64_t)s_row[u] * K; },
+    stg.load(NB, LPR * BPL, n_tok, MTR, [&](int u) { return in + (int64_t)s_row[rb + u] * K; },
              [&](int) { return 1.0f; });
     stg.store(s_x);
     lds_barrier();
@@ -172,10 +202,10 @@ __global__ void __launch_bounds__(kGemvThreads, 2) gemv_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ in,
     float* __restrict__ out, int H, int F, int E, int S, int k, int T, int tch) {
-  extern __shared__ uint32_t s_x[];           // MT tokens x LPR*BPL blocks x kXStride dwords
+  extern __shared__ __align__(16) uint32_t s_x[];   // MT tokens x LPR*BPL blocks x kXStride dwords
   __shared__ uint32_t s_tab[256];
   __shared__ int s_expert, s_chunk;
-  __shared__ int s_row[MT];                   // row index of each staged token in `in`
+  __shared__ int s_row[2 * MT];               // row index of each staged token in `in`
 
   const int tid = threadIdx.x;
   s_tab[tid] = pair_table_entry(tid);
@@ -251,7 +281,12 @@ static void launch_one(dim3 grid, hipStream_t s, const uint8_t* bank, int64_t st
   // chunk an expert beyond rows / tch
   const int tch = (T > 4 && T <= 16) ? kBatchChunk : T;
   const int rows = T * (sh.k + sh.S);
-  grid.y += (rows + tch - 1) / tch;
+  // items = sum over the (at most grid.y) bins with slots of ceil(m_e / tch)
+  //       <= (rows + bins * (tch - 1)) / tch, and <= rows (an item holds a slot)
+  const int64_t bins = grid.y;
+  const int64_t bound = std::min<int64_t>(
+      {bins + (rows + tch - 1) / tch, (rows + bins * (tch - 1)) / tch, (int64_t)rows});
+  grid.y = (unsigned)bound;
   hipLaunchKernelGGL((gemv_kernel<LPR, BPL, MT, GU>), grid, dim3(kGemvThreads), lds, s, bank,
                      stride, offsets, sp, in, out, sh.H, sh.F, sh.E, sh.S, sh.k, T, tch);
 }
