@@ -249,8 +249,11 @@ def _oracle_rows(wl, e, which, rows):
     return iq4nl.dequantize_matrix(iq4nl.quantize_matrix(w), len(rows), w.shape[1])
 
 
+# T = 40: one chunk of all 40 slots an expert, so the shared expert runs 20 two-token tiles
+# (the tiles past the first two read their token rows on their own)
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("xing4_decode", 1), ("xing4_decode", 16),
-                                    ("qwen3next_like", 2), ("dsv41_like", 3)])
+                                    ("xing4_decode", 40), ("qwen3next_like", 2),
+                                    ("dsv41_like", 3)])
 @pytest.mark.parametrize("stage", ["gate_up", "down"])
 def test_gemv_against_oracle(name, T, stage):
     wl = WORKLOADS[name]
