@@ -15,8 +15,23 @@ constexpr int kBlockBytes = 18;   // bytes per block
 
 // The 16-entry signed int8 non-linear codebook (16-level Lloyd-Max levels of a unit normal,
 // scaled to a largest magnitude of 127).
-static __constant__ int8_t kCodebook[16] = {
+constexpr int8_t kCodebookValues[16] = {
     -127, -96, -75, -58, -44, -31, -18, -6, 6, 18, 31, 44, 58, 75, 96, 127};
+
+constexpr uint64_t codebook_bytes(int first) {
+  uint64_t r = 0;
+  for (int i = 0; i < 8; ++i) r |= (uint64_t)(uint8_t)kCodebookValues[first + i] << (8 * i);
+  return r;
+}
+
+// Codebook value q (0..15) without a memory read: the 16 bytes live in two 64-bit literals.
+// (A table in memory would be a load, and a wave's loads complete in issue order: waiting
+// for it would also wait for every load issued before it.)
+__device__ __forceinline__ int codebook_at(int q) {
+  constexpr uint64_t lo = codebook_bytes(0), hi = codebook_bytes(8);
+  const uint64_t v = (q & 8) ? hi : lo;
+  return (int)(int8_t)(uint8_t)(v >> (8 * (q & 7)));
+}
 
 // bf16 bit pattern of a small integer (exact: |v| <= 127 needs 7 significant bits).
 __device__ __forceinline__ uint32_t bf16_bits_of_int(int v) {
@@ -26,7 +41,7 @@ __device__ __forceinline__ uint32_t bf16_bits_of_int(int v) {
 // Byte table: entry b = (bf16(c[b & 15]) | bf16(c[b >> 4]) << 16), i.e. one code byte of a
 // block (indices q_j low, q_{j+16} high) to the bf16 pair of its two codebook values.
 __device__ __forceinline__ uint32_t pair_table_entry(int b) {
-  return bf16_bits_of_int(kCodebook[b & 15]) | (bf16_bits_of_int(kCodebook[b >> 4]) << 16);
+  return bf16_bits_of_int(codebook_at(b & 15)) | (bf16_bits_of_int(codebook_at(b >> 4)) << 16);
 }
 
 // The 18 bytes of block number `blk` of a row that starts 4-byte aligned, read as five

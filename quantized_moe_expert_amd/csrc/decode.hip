@@ -383,6 +383,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   __shared__ int s_off[1025];
   __shared__ int s_act[1024];
   __shared__ int s_nact;
+  __shared__ float s_cw[2 * kDecThreads];        // gating weights w[0 .. P)
+  __shared__ int s_cps[2 * kDecThreads];         // pair_slot[0 .. P)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * k, NBIN = E + S;
@@ -392,12 +394,32 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   uint32_t* s_x = s_dyn;                                   // rows_total x NBP x kXStride
   float* s_o = reinterpret_cast<float*>(s_dyn + rows_total * NBP * kXStride);  // R x rows
 
+  // the codebook pair table first: its two reads of the codebook are waited on at once, and
+  // loads complete in issue order, so any load issued before them would be waited on too
+  s_tab[tid] = pair_table_entry(tid);
   // load order: the route table (the routed weight addresses wait on it), every slot's h,
   // then the shared expert's weights, which need no route table (loads complete in order)
   int ov[(1025 + kDecThreads - 1) / kDecThreads];
 #pragma unroll
   for (int j = 0; j < (1025 + kDecThreads - 1) / kDecThreads; ++j)
     ov[j] = offsets[min(tid + kDecThreads * j, NBIN)];
+  // the combine's inputs, read now rather than after the dot products (they were written by
+  // earlier launches); relaxed atomic reads, so that the compiler keeps them here instead of
+  // sinking them to their use.  P <= 2 * kDecThreads and T * R <= kDecThreads are checked on
+  // the host; the reads are clamped and unconditional
+  float cwv[2];
+  int cpsv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = min(tid + kDecThreads * j, P - 1);
+    cwv[j] = __hip_atomic_load(w + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    cpsv[j] = __hip_atomic_load(pair_slot + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  const int rl_c = tid % R, t_c = min(tid / R, T - 1);
+  // (read through a pointer that is always valid, then selected: no branch around the load)
+  const float* res_p =
+      residual ? residual + (int64_t)t_c * H + min((int)blockIdx.x * R + rl_c, H - 1) : w;
+  const float res_v = __hip_atomic_load(res_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   Stager<UPT> stg;
   stg.load(NB, NBP, rows_total, rows_total,
            [&](int u) -> const float* { return h + (int64_t)u * F; }, [&](int) { return 1.0f; });
@@ -426,10 +448,14 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   for (int d = 0; d < kDownRing; ++d)
     if (d < pre) load_rows(E, d, ring[d]);
 
-  s_tab[tid] = pair_table_entry(tid);
 #pragma unroll
   for (int j = 0; j < (1025 + kDecThreads - 1) / kDecThreads; ++j)
     if (tid + kDecThreads * j <= NBIN) s_off[tid + kDecThreads * j] = ov[j];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    s_cw[tid + kDecThreads * j] = cwv[j];
+    s_cps[tid + kDecThreads * j] = cpsv[j];
+  }
   lds_barrier();
   // compact list of experts with slots: the shared expert, then the routed ones in index order
   if (wave == 0) {
@@ -484,16 +510,17 @@ __global__ void __launch_bounds__(kDecThreads) decode_down_combine_kernel(
   __syncthreads();
 
   // combine in fixed order: routed j = 0..k-1, then shared experts, then the residual
-  for (int i = tid; i < T * R; i += kDecThreads) {
-    const int t = i / R, rl = i % R;
+  if (tid < T * R) {
+    const int t = tid / R, rl = tid % R;
     const int r = r0 + rl;
-    if (r >= H) continue;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j)
-      acc = fmaf(w[t * k + j], s_o[rl * rows_total + pair_slot[t * k + j]], acc);
-    for (int sidx = 0; sidx < S; ++sidx) acc += s_o[rl * rows_total + P + sidx * T + t];
-    if (residual) acc += residual[(int64_t)t * H + r];
-    y[(int64_t)t * H + r] = acc;
+    if (r < H) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j)
+        acc = fmaf(s_cw[t * k + j], s_o[rl * rows_total + s_cps[t * k + j]], acc);
+      for (int sidx = 0; sidx < S; ++sidx) acc += s_o[rl * rows_total + P + sidx * T + t];
+      if (residual) acc += res_v;
+      y[(int64_t)t * H + r] = acc;
+    }
   }
 }
 
@@ -580,7 +607,10 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
                           const float* h, const int32_t* off, const int32_t* ps, const float* w,
                           int T, const Shape& sh, const float* residual, float* y) {
   // rows per workgroup 4 * NRP * RPP: about 16 for every group width, 8 for one-block rows of
-  // 32 lanes (FFN 1024: twice the workgroups, 448 over 256 CUs, measured faster)
+  // 32 lanes (FFN 1024: twice the workgroups, 448 over 256 CUs, measured faster).  The
+  // combine's inputs are read by one thread each: T * k <= 2 * kDecThreads and T * R <=
+  // kDecThreads (R <= 64)
+  if ((int64_t)T * sh.k > 2 * kDecThreads || T * 64 > kDecThreads) return false;
 #define DN(L, B, N) \
   if (gm.lpr == L && gm.bpl == B) { launch_down<L, B, N>(s, bank, stride, h, off, ps, w, T, sh, residual, y); return true; }
   DN(64, 1, 4) DN(64, 2, 4) DN(64, 3, 4) DN(64, 4, 4) DN(32, 1, 1) DN(32, 2, 2) DN(32, 3, 2)

@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, c16 = lane & 15;
 
-  s_tab[tid] = make_float2((float)kCodebook[tid & 15], (float)kCodebook[tid >> 4]);
+  s_tab[tid] = make_float2((float)codebook_at(tid & 15), (float)codebook_at(tid >> 4));
 
   // ---- tile prefix over experts: s_pref[e] = sum_{e' <= e} ceil(m_e' / kBM) ----
   const int nbins = E + S;

@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__
   const float d = __half2float(dh);
   float mid[15];
 #pragma unroll
-  for (int j = 0; j < 15; ++j) mid[j] = d * (0.5f * (float)(kCodebook[j] + kCodebook[j + 1]));
+  for (int j = 0; j < 15; ++j) mid[j] = d * (0.5f * (float)(codebook_at(j) + codebook_at(j + 1)));
   uint32_t q[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -64,8 +64,8 @@ __global__ void __launch_bounds__(256) dequantize_kernel(const uint8_t* __restri
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t byte = (two >> (8 * h)) & 0xFF;
-      v[2 * j + h] = d * (float)kCodebook[byte & 15];
-      v[2 * j + h + 16] = d * (float)kCodebook[byte >> 4];
+      v[2 * j + h] = d * (float)codebook_at(byte & 15);
+      v[2 * j + h + 16] = d * (float)codebook_at(byte >> 4);
     }
   }
 #pragma unroll
