@@ -110,10 +110,43 @@ def traffic(kernel, root):
     return None
 
 
+def counter_summary(csv_path, command, cu_count=256, xcds=8):
+    """Per kernel: the mean per dispatch of every counter in a rocprofv3 --pmc CSV, and the
+    ratios these counters define (LDS bank-conflict share of LDS cycles, MFMA busy share of
+    SIMD cycles, LDS active share of CU cycles).  GRBM_GUI_ACTIVE reads as the sum over the
+    XCDs (8 x the kernel's cycles), so the elapsed cycles are that value / xcds."""
+    per = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        per[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = [f"command: {command}", ""]
+    for k in sorted(per):
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        n = max(len(v) for v in per[k].values())
+        out.append(f"kernel {k}: dispatches {n}")
+        for name in sorted(c):
+            out.append(f"  {name:28s} {c[name]:.4g}")
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"]:
+            out.append(f"  bank-conflict cycles / LDS active cycles: "
+                       f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.3f}")
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if cyc:
+            out.append(f"  elapsed cycles (GRBM_GUI_ACTIVE / {xcds}): {cyc:.4g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and cyc:
+            out.append(f"  MFMA busy / (elapsed cycles x {4 * cu_count} SIMDs): "
+                       f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 4 * cu_count):.3f}")
+        if "SQ_LDS_IDX_ACTIVE" in c and cyc:
+            out.append(f"  LDS active / (elapsed cycles x {cu_count} CUs): "
+                       f"{c['SQ_LDS_IDX_ACTIVE'] / (cyc * cu_count):.3f}")
+        out.append("")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         sys.stdout.write(stats_summary(sys.argv[2], sys.argv[3]))
     elif sys.argv[1] == "pmc":
         sys.stdout.write(pmc_summary(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif sys.argv[1] == "counters":
+        sys.stdout.write(counter_summary(sys.argv[2], sys.argv[3]))
     else:
         raise SystemExit(__doc__)
