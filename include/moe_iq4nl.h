@@ -103,11 +103,7 @@ int32_t moe_last_hip_error(void);
  * moe_grouped_gemm_iq4nl, moe_decode_layer and moe_decode_chain need for n_tokens tokens of
  * this layer shape (one size covers all calls).  Workspace layout:
  *   bytes 0..3   after moe_permute, the number of route pairs it sanitised (int32)
- *   bytes 4..7   status word of moe_decode_chain (uint32, sticky; 0 = no error)
- *   bytes 256..  moe_decode_chain's control counters: they must be ZERO before the first
- *                moe_decode_chain call on a workspace (allocate it zero-filled) and every
- *                completed call leaves them zero; no other entry point writes them
- *   the rest     scratch */
+ *   bytes 256..  scratch (contents are not preserved between calls) */
 moe_status moe_workspace_size(const moe_desc *desc, int32_t n_tokens, size_t *bytes);
 
 /* Encode fp32 weights as IQ4_NL: w holds n_blocks groups of 32 consecutive weights; out
@@ -225,23 +221,17 @@ typedef struct moe_layer {
 
 #define MOE_CHAIN_MAX_LAYERS 64
 
-/* Decode step of a stack of layers, 1 <= T <= 16 tokens, in ONE persistent launch (PocketLLM
- * page, "Known limitations": a decode step bound by its launch count; Red Lite "1. The idea":
- * the whole token routed on the GPU, no host round trip between layers).  For l = 0 ..
- * n_layers-1, in place:
+/* Decode step of a stack of layers, 1 <= T <= 16 tokens, with no host round trip between
+ * layers (PocketLLM page, "Known limitations": a decode step bound by its launch count; Red
+ * Lite "1. The idea": the whole token routed on the GPU).  For l = 0 .. n_layers-1, in place:
  *   x <- x + MoE_l(xn),  xn = norm_eps >= 0 ? x / sqrt(mean(x^2) + norm_eps) : x  (per row)
- * with MoE_l as in moe_decode_layer (routing of moe_route, fp32 GEMV arithmetic of
- * moe_expert_gemv_iq4nl, fixed-order combine of moe_combine) on layers[l].
+ * with MoE_l as in moe_decode_layer on layers[l], enqueued as that entry point's launches,
+ * layer after layer, on one stream (capture the call in a HIP graph to replay a whole step).
  *   layers    host array of n_layers (<= MOE_CHAIN_MAX_LAYERS) entries, read during the call
  *   x         [T, H] fp32, in/out
  *   topk_ids, topk_w: both NULL, or [n_layers, T, k] outputs of every layer's route
- *   ws        >= moe_workspace_size(desc, T) bytes, 256-byte aligned; its control counters
- *             (see moe_workspace_size) must be zero before the first call
- * Work inside the launch is a ticket queue of router, gate/up and down items in layer order;
- * every wait inside it is bounded: should one expire, bit 0 of the workspace status word is
- * set and x is invalid (the launch still completes).  Calls sharing a workspace must be
- * ordered on one stream.  Shapes the persistent kernel has no configuration for run as three
- * launches a layer, with the same results contract. */
+ *   ws        >= moe_workspace_size(desc, T) bytes, 256-byte aligned
+ * Every layer's bank and router are checked before anything is enqueued. */
 moe_status moe_decode_chain(const moe_desc *desc, const moe_layer *layers, int32_t n_layers,
                             float *x, int32_t n_tokens, float norm_eps, int32_t *topk_ids,
                             float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream);

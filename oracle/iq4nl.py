@@ -114,8 +114,10 @@ def quantize_blocks(w: np.ndarray) -> np.ndarray:
     d = d16.astype(np.float64)
     c = np.asarray(CODEBOOK, dtype=np.float64)
     mids = (c[:-1] + c[1:]) / 2.0                                     # 15 half-integers
-    thr = d[..., None, None] * mids                                   # exact
-    q = np.sum(thr < w.astype(np.float64)[..., :, None], axis=-1).astype(np.uint8)
+    wd = w.astype(np.float64)
+    q = np.zeros(w.shape, dtype=np.uint8)
+    for m in mids:                                  # q = number of midpoints below w
+        q += (d[..., None] * m < wd)                # d * m exact in fp64
     return pack_blocks(d_bits, q)
 
 

@@ -22,7 +22,7 @@ LIBS = {
     os.path.join(PKG, "libmoe_iq4nl.so"): [
         os.path.join(PKG, "csrc", f) for f in
         ("api.hip", "quant.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip",
-         "combine.hip", "decode.hip", "chain.hip")],
+         "combine.hip", "decode.hip")],
     os.path.join(ROOT, "synth", "libmoe_synth.so"): [
         os.path.join(ROOT, "synth", "csrc", "synth.hip")],
 }

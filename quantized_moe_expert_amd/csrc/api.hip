@@ -30,12 +30,9 @@ using moe::Shape;
 
 namespace {
 
-// Workspace: bytes 0..3 the sanitised-pair count of moe_permute, 4..7 the status word of
-// moe_decode_chain, 256.. the chain's control counters, then scratch.
-constexpr size_t kStatusOffset = 4;
-constexpr size_t kControlOffset = 256;
-constexpr size_t kHeaderBytes = kControlOffset + moe::kChainControlBytes;
-static_assert(kHeaderBytes % 256 == 0, "scratch alignment");
+// Workspace: bytes 0..3 the sanitised-pair count of moe_permute, then (from byte 256)
+// scratch.
+constexpr size_t kHeaderBytes = 256;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -104,39 +101,12 @@ DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
   return L;
 }
 
-// Decode chain: header | kChainMaxLayers blocks, one a layer, each
-//   x | logits | rscale | w | pair_slot | slot_tok | act | h
-struct ChainLayout {
-  size_t x, logits, rscale, w, ps, slot_tok, act, h, block, total;
-};
-
-ChainLayout chain_layout(const moe_desc* d, int32_t T) {
-  const size_t P = (size_t)T * d->top_k;
-  const size_t rows = P + (size_t)T * d->n_shared;
-  ChainLayout L;
-  size_t off = 0;
-  L.x = off; off += align256((size_t)T * d->hidden * 4);
-  L.logits = off; off += align256((size_t)T * d->n_experts * 4);
-  L.rscale = off; off += align256((size_t)T * 4);
-  L.w = off; off += align256(P * 4);
-  L.ps = off; off += align256(P * 4);
-  L.slot_tok = off; off += align256(rows * 4);
-  L.act = off; off += align256((1 + 3 * (size_t)d->n_experts) * 4);
-  L.h = off; off += align256(rows * d->ffn * 4);
-  L.block = off;
-  L.total = kHeaderBytes + (size_t)moe::kChainMaxLayers * off;
-  return L;
-}
-
 size_t ws_bytes_for(const moe_desc* d, int32_t T) {
   const size_t route_part = (size_t)moe::route_splits(shape_of(d), T, ~size_t(0)) * T *
                            d->n_experts * 4;
   size_t b = kHeaderBytes + logits_bytes(d, T) +
              align256(std::max(moe::permute_scratch_bytes(shape_of(d), T), route_part));
-  if (T <= moe::kDecodeMaxTokens) {
-    b = std::max(b, decode_layout(d, T).total);
-    b = std::max(b, chain_layout(d, T).total);
-  }
+  if (T <= moe::kDecodeMaxTokens) b = std::max(b, decode_layout(d, T).total);
   return b;
 }
 
@@ -360,24 +330,7 @@ moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32
   const Shape sh = shape_of(desc);
   uint8_t* b = static_cast<uint8_t*>(ws);
   const size_t P = (size_t)n_tokens * desc->top_k;
-  if (moe::chain_supported(sh, n_tokens)) {
-    const ChainLayout L = chain_layout(desc, n_tokens);
-    moe::ChainLayer lay[MOE_CHAIN_MAX_LAYERS];
-    for (int32_t l = 0; l < n_layers; ++l)
-      lay[l] = moe::ChainLayer{layers[l].bank.base, layers[l].bank.expert_stride,
-                               layers[l].w_router, layers[l].bias};
-    moe::ChainScratch sc;
-    sc.control = b + kControlOffset;
-    sc.status = reinterpret_cast<uint32_t*>(b + kStatusOffset);
-    sc.layers = b + kHeaderBytes;
-    sc.layer_stride = (int64_t)L.block;
-    sc.off_x = (int32_t)L.x; sc.off_logits = (int32_t)L.logits; sc.off_rscale = (int32_t)L.rscale;
-    sc.off_w = (int32_t)L.w; sc.off_ps = (int32_t)L.ps; sc.off_slot_tok = (int32_t)L.slot_tok;
-    sc.off_act = (int32_t)L.act; sc.off_h = (int32_t)L.h;
-    return hip_status(moe::launch_decode_chain(sh, lay, n_layers, x, n_tokens, norm_eps,
-                                               topk_ids, topk_w, sc, stream));
-  }
-  // shapes without a persistent configuration: three launches a layer
+  // every layer through the fused decode layer, the route table kept on the device
   const DecodeLayout L = decode_layout(desc, n_tokens);
   moe::DecodeScratch sc;
   sc.logits = reinterpret_cast<float*>(b + L.logits);

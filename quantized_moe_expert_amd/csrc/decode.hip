@@ -580,7 +580,8 @@ static bool dispatch_up(DecGeom gm, dim3 grid, hipStream_t s, const uint8_t* ban
 #define UP(L, B) \
   if (gm.lpr == L && gm.bpl == B) { launch_up<L, B, MT, P>(grid, s, bank, stride, x, rs, logits, T, sh, ids, w, off, sp, ps, h, T); return true; }
   UP(64, 1) UP(64, 2) UP(64, 3) UP(64, 4) UP(32, 1) UP(32, 2) UP(32, 3) UP(32, 4)
-  UP(16, 1) UP(16, 2) UP(16, 3) UP(16, 4) UP(8, 1) UP(8, 2) UP(4, 1) UP(4, 2)
+  UP(16, 1) UP(16, 2) UP(16, 3) UP(16, 4) UP(8, 1) UP(8, 2) UP(8, 3) UP(8, 4) UP(4, 1)
+  UP(4, 2) UP(4, 3) UP(4, 4)
 #undef UP
   return false;
 }
@@ -615,7 +616,7 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
   if (gm.lpr == L && gm.bpl == B) { launch_down<L, B, N>(s, bank, stride, h, off, ps, w, T, sh, residual, y); return true; }
   DN(64, 1, 4) DN(64, 2, 4) DN(64, 3, 4) DN(64, 4, 4) DN(32, 1, 1) DN(32, 2, 2) DN(32, 3, 2)
   DN(32, 4, 2) DN(16, 1, 1) DN(16, 2, 1) DN(16, 3, 1) DN(16, 4, 1) DN(8, 1, 1) DN(8, 2, 1)
-  DN(4, 1, 1) DN(4, 2, 1)
+  DN(8, 3, 1) DN(8, 4, 1) DN(4, 1, 1) DN(4, 2, 1) DN(4, 3, 1) DN(4, 4, 1)
 #undef DN
   return false;
 }

@@ -78,28 +78,6 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
                                float eps, const float* residual, float* y, DecodeScratch sc,
                                int stages, hipStream_t s);
 
-// Persistent multi-layer decode (one launch for a stack of layers, T <= 16).
-constexpr int kChainMaxLayers = 64;
-struct ChainLayer {
-  const uint8_t* bank;
-  int64_t stride;
-  const float* wr;
-  const float* bias;
-};
-struct ChainScratch {
-  void* control;          // kChainControlBytes, zero before the first launch, left zero
-  uint32_t* status;       // bit 0 set when a bounded wait expired (sticky)
-  void* layers;           // kChainMaxLayers blocks of layer_stride bytes, one per layer
-  int64_t layer_stride;
-  // byte offsets inside a layer block (each 256-byte aligned)
-  int32_t off_x, off_logits, off_rscale, off_w, off_ps, off_slot_tok, off_act, off_h;
-};
-constexpr size_t kChainControlBytes = 2 * 128 + (size_t)kChainMaxLayers * 4 * 128;
-bool chain_supported(const Shape& sh, int T);
-hipError_t launch_decode_chain(const Shape& sh, const ChainLayer* layers, int n_layers,
-                               float* x, int T, float eps, int32_t* ids_out, float* w_out,
-                               const ChainScratch& sc, hipStream_t s);
-
 int device_cu_count();
 
 }  // namespace moe

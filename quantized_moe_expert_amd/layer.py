@@ -37,7 +37,6 @@ class LayerBuffers:
         self.sorted_pairs = torch.empty(max(T * s.top_k, 1), **i32)
         self.pair_slot = torch.empty(max(T * s.top_k, 1), **i32)
         self.ws_bytes = moe_workspace_size(self.desc, T)
-        # zero-filled: moe_decode_chain's control counters start at zero
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
         if prefill:
             self.x_perm = torch.empty((rows, s.hidden), dtype=torch.bfloat16, device=device)
@@ -104,7 +103,7 @@ def decode_chain_step(buf, x, layers, eps=1e-6, fused=True):
 
 
 def decode_chain(buf, x, layers, eps=1e-6, ids=None, w=None):
-    """x <- x + MoE_l(rmsnorm(x)) for every layer, in place, in ONE moe_decode_chain launch.
+    """x <- x + MoE_l(rmsnorm(x)) for every layer, in place, in ONE moe_decode_chain call.
 
     layers: list of (w_router, bias, bank) or the ctypes array of ``make_layers``;
     ids / w: optional [L, T, k] outputs of every layer's route."""
@@ -112,11 +111,6 @@ def decode_chain(buf, x, layers, eps=1e-6, ids=None, w=None):
         layers = make_layers([(bank, wr, bias) for (wr, bias, bank) in layers])
     moe_decode_chain(buf.desc, layers, len(layers), x, buf.T, eps, ids, w, buf.ws, buf.ws_bytes)
     return x
-
-
-def chain_status(buf):
-    """Status word of moe_decode_chain in the workspace (0: no bounded wait expired)."""
-    return int(buf.ws[4:8].view(torch.int32).item())
 
 
 # ---- expert banks from the seeded generator ----------------------------------------------

@@ -51,7 +51,7 @@ def test_workspace_size_grows_with_tokens_and_covers_the_header():
     d = M.make_desc(3584, 1024, 64, 4, 1, M.MOE_GATING_SIGMOID, 1, 16)
     sizes = [M.moe_workspace_size(d, T) for T in (1, 2, 16)]
     assert sizes == sorted(sizes)
-    assert sizes[0] >= 256 + 2 * 128 + 64 * 4 * 128       # header + chain control counters
+    assert sizes[0] >= 256                                 # header (sanitised-pair count)
 
 
 @pytest.mark.parametrize("field,value", [("hidden", 100), ("ffn", 32), ("top_k", 0),

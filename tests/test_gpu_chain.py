@@ -1,9 +1,8 @@
-"""GPU parity of moe_decode_chain: a stack of decode layers in one persistent launch.
+"""GPU parity of moe_decode_chain: a stack of decode layers in one call.
 
 Each layer is x <- x + MoE_l(rmsnorm(x)).  Checked against the oracle's chain (fp64) on short
 stacks, against the per-layer entry point on the full 38-layer stack, for bit-identical
-reruns and HIP-graph replays, for the control counters being left at zero and the status
-word staying clear, and for the host-side argument checks.
+reruns and HIP-graph replays, and for the host-side argument checks.
 """
 import numpy as np
 import pytest
@@ -19,7 +18,6 @@ from .helpers import REL_L2_GEMV, assert_close, desc_of, oracle_bank, topk_gap
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
-CTRL = slice(256, 256 + 2 * 128 + 64 * 4 * 128)    # the chain's control counters in ws
 
 
 def _layers(wl, n):
@@ -49,12 +47,6 @@ def _oracle_chain(wl, T, n):
     return x, np.stack(ids_all), np.stack(gaps)
 
 
-def _assert_clean(buf):
-    torch.cuda.synchronize()
-    assert L.chain_status(buf) == 0
-    assert int(buf.ws[CTRL].count_nonzero().item()) == 0
-
-
 @pytest.mark.parametrize("name,T,n", [("tiny", 4, 3), ("xing4_decode", 1, 2),
                                       ("xing4_decode", 2, 2), ("qwen3next_like", 1, 2),
                                       ("qwen3next_like", 2, 2)])
@@ -67,7 +59,7 @@ def test_chain_vs_oracle(name, T, n):
     ids = torch.empty((n, T, s.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((n, T, s.top_k), dtype=torch.float32, device="cuda")
     L.decode_chain(buf, x, layers, EPS, ids, w)
-    _assert_clean(buf)
+    torch.cuda.synchronize()
     ref, ref_ids, gaps = _oracle_chain(wl, T, n)
     assert gaps.min() > 1e-4, "fixture has a routing near-tie"
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
@@ -89,20 +81,20 @@ def test_chain_38_layers_vs_per_layer_path():
         L.decode_chain_step(buf1, xr, [lay], EPS)
         ref_ids.append(buf1.ids.clone())
     ref_ids = torch.stack(ref_ids)
-    # one launch
+    # one call for the whole stack
     buf = L.LayerBuffers(s, T)
     x = x0.clone()
     ids = torch.empty((wl.layers, T, s.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((wl.layers, T, s.top_k), dtype=torch.float32, device="cuda")
     L.decode_chain(buf, x, layers, EPS, ids, w)
-    _assert_clean(buf)
+    torch.cuda.synchronize()
     assert torch.equal(ids, ref_ids)
     assert_close(x.cpu().numpy(), xr.cpu().numpy().astype(np.float64), REL_L2_GEMV,
                  "chain vs per-layer, 38 layers")
-    # rerun: bit-identical, counters reset again
+    # rerun: bit-identical
     x2 = x0.clone()
     L.decode_chain(buf, x2, layers, EPS)
-    _assert_clean(buf)
+    torch.cuda.synchronize()
     assert torch.equal(x2, x)
 
 
@@ -116,7 +108,7 @@ def test_chain_graph_replay():
     buf = L.LayerBuffers(s, T)
     eager = x0.clone()
     L.decode_chain(buf, eager, arr, EPS)
-    _assert_clean(buf)
+    torch.cuda.synchronize()
     xg = x0.clone()
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -132,15 +124,14 @@ def test_chain_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(xg, eager)
-        _assert_clean(buf)
+        torch.cuda.synchronize()
         junk = torch.randn(1000, device="cuda").sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
         del junk
 
 
-def test_chain_unconfigured_shape_uses_per_layer_launches():
-    # 16 tokens of the 3584/1024 shape: h of every slot does not fit one workgroup's LDS,
-    # so the entry point runs three launches a layer; results equal the per-layer path
+def test_chain_sixteen_tokens_equals_per_layer_path():
+    # 16 tokens of the 3584/1024 shape: the stack call equals the per-layer calls bit for bit
     wl = XING4_DECODE
     s = wl.shape
     T = 16

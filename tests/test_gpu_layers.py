@@ -14,7 +14,8 @@ import quantized_moe_expert_amd as M
 from quantized_moe_expert_amd import layer as L
 from oracle import moe as omoe
 from synth import generator as G
-from synth.configs import WORKLOADS, TINY, XING4_DECODE
+from synth.configs import (WORKLOADS, TINY, XING4_DECODE, LayerShape, SIGMOID,
+                           Workload)
 
 from .helpers import (REL_L2_GEMV, REL_L2_MFMA, assert_close, desc_of, oracle_bank,
                       oracle_layer, topk_gap)
@@ -55,9 +56,9 @@ def test_tiny_layer_full(prefill):
     assert_close(y, ref, REL_L2_MFMA if prefill else REL_L2_GEMV, f"tiny prefill={prefill}")
 
 
-@pytest.mark.parametrize("name,T,n_check", [("xing4_decode", 1, 1), ("xing4_decode", 16, 2),
+@pytest.mark.parametrize("name,T,n_check", [("xing4_decode", 1, 1), ("xing4_decode", 16, 16),
                                             ("qwen3next_like", 1, 1), ("qwen3next_like", 2, 2),
-                                            ("dsv41_like", 16, 1)])
+                                            ("dsv41_like", 16, 4)])
 def test_decode_layer_full_size(name, T, n_check):
     wl = WORKLOADS[name]
     y, buf, _ = _gpu_layer(wl, T, prefill=False)
@@ -90,7 +91,7 @@ def test_prefill_layer_full_size(name, T, n_check):
 
 
 @pytest.mark.parametrize("name,T,n_check", [("tiny", 4, 4), ("xing4_decode", 1, 1),
-                                            ("xing4_decode", 16, 2), ("qwen3next_like", 1, 1),
+                                            ("xing4_decode", 16, 16), ("qwen3next_like", 1, 1),
                                             ("qwen3next_like", 2, 2), ("dsv41_like", 16, 1),
                                             # ragged batches: partial token tiles and chunks
                                             ("xing4_decode", 3, 3), ("xing4_decode", 7, 2),
@@ -120,6 +121,33 @@ def test_fused_decode_layer_full_size(name, T, n_check):
     ref, parts = oracle_layer(wl, 0, xh[toks], return_parts=True)
     assert np.array_equal(ids.cpu().numpy()[toks], parts["ids"])
     assert_close(y.cpu().numpy()[toks], ref, REL_L2_GEMV, f"fused {name} T={T}")
+
+
+# row lengths whose lane geometry is 4 or 8 lanes of 3 blocks (hidden 384 and 768, FFN 384)
+ODD_SHAPES = {
+    "h384_f384": Workload(name="h384_f384", cfg_id=7,
+                          shape=LayerShape(hidden=384, ffn=384, n_experts=16, top_k=3, n_shared=1,
+                                           gating=SIGMOID, renormalize=1), layers=1),
+    "h768_f384": Workload(name="h768_f384", cfg_id=8,
+                          shape=LayerShape(hidden=768, ffn=384, n_experts=16, top_k=2, n_shared=1,
+                                           gating=SIGMOID, renormalize=1), layers=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ODD_SHAPES))
+@pytest.mark.parametrize("T", [1, 3, 9])
+def test_fused_decode_layer_odd_row_lengths(name, T):
+    wl = ODD_SHAPES[name]
+    bank_t, bank = L.make_bank(wl, 0)
+    wr, bias = L.make_router(wl, 0)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(wl.shape, T)
+    y = L.decode_layer_fused(buf, x, wr, bias, bank, norm_eps=1e-6).clone()
+    torch.cuda.synchronize()
+    xh = omoe.rmsnorm(G.activations(wl, T), 1e-6)
+    ref, parts = oracle_layer(wl, 0, xh, return_parts=True)
+    assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
+    assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"{name} T={T}")
 
 
 def test_fused_decode_rejects_large_batches():

@@ -3,6 +3,7 @@ scalar brute force.  Pages: PocketLLM "Xing4.0-29B-A4B" (sections "Overview", "W
 server", "Where the detail is"); "Running Qwen Flash-Next NVFP4 in vLLM" (route validation).
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -243,3 +244,42 @@ def test_chain_one_layer_and_two_layers():
     assert np.allclose(y1, x + moe.moe_layer(moe.rmsnorm(x), wr, b, bank, stride, desc))
     y2 = moe.chain(x, [(wr, b, bank, stride)] * 2, desc)
     assert np.allclose(y2, y1 + moe.moe_layer(moe.rmsnorm(y1), wr, b, bank, stride, desc))
+
+
+def _scalar_rmsnorm(row, eps):
+    """x / sqrt(mean(x^2) + eps) of one row, written as loops."""
+    ss = 0.0
+    for v in row:
+        ss += v * v
+    r = 1.0 / math.sqrt(ss / len(row) + eps)
+    return [v * r for v in row]
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.25])
+def test_chain_against_scalar_twin_three_distinct_layers(eps):
+    """The chain glue (weight-free RMSNorm on each layer's input, residual of the un-normalised
+    x, layers in order) against the scalar-loop twin of the layer, chained by hand over three
+    layers with different weights, routers and biases.  eps = 0.25 on small activations makes
+    the norm's epsilon visible; a wrong eps, norm placement, residual or layer order fails."""
+    rng = np.random.default_rng(16)
+    H, F, E, k, T = 64, 32, 4, 2, 3
+    layers = []
+    for l in range(3):
+        desc, bank, stride, _, wr, b = _rand_layer(rng, H, F, E, k, T=T, bias=(l != 1))
+        layers.append((wr, b, bank, stride))
+    x = (rng.standard_normal((T, H)) * 0.3).astype(np.float32)
+    got = moe.chain(x, layers, desc, eps)
+    ref = []
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        for (wr, b, bank, stride) in layers:
+            xn = _scalar_rmsnorm(xt, eps)
+            y = bruteforce.layer([xn], wr.tolist(), None if b is None else b.tolist(),
+                                 bank.tolist(), stride, H, F, E, k, desc.gating,
+                                 desc.renormalize)[0]
+            xt = [xt[i] + y[i] for i in range(H)]
+        ref.append(xt)
+    assert np.allclose(got, np.asarray(ref), rtol=1e-12, atol=1e-12)
+    # the layers do not commute: the reversed stack gives a different result
+    rev = moe.chain(x, layers[::-1], desc, eps)
+    assert not np.allclose(rev, got, rtol=1e-6, atol=1e-6)
