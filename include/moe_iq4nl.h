@@ -65,7 +65,8 @@ typedef enum {
     MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() reported    */
     MOE_ERR_UNSUPPORTED = 4,   /* an enum value or feature this build does not support    */
     MOE_ERR_HIP = 5,           /* a HIP launch failed                                     */
-    MOE_ERR_ALIGNMENT = 6      /* a pointer or stride violates the alignment contract     */
+    MOE_ERR_ALIGNMENT = 6,     /* a pointer or stride violates the alignment contract     */
+    MOE_ERR_SCRATCH_LIMIT = 7  /* more scratch than moe_decode_layer_noalloc's array holds */
 } moe_status;
 
 typedef enum { MOE_GATING_SIGMOID = 0, MOE_GATING_SOFTMAX = 1 } moe_gating;
@@ -211,6 +212,29 @@ moe_status moe_decode_layer(const moe_desc *desc, const moe_bank *bank, const fl
                             const float *bias, const float *x, int32_t n_tokens, float norm_eps,
                             const float *residual, float *y, int32_t *topk_ids, float *topk_w,
                             int32_t stages, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of moe_decode_layer, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same checks, launches and results as moe_decode_layer, with the workspace replaced by a
+ * fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds in device memory on
+ * each GPU it runs on, from that GPU's first call until the process ends.  Nothing is
+ * allocated or freed by the call.  Inputs and outputs are the caller's, as in
+ * moe_decode_layer.
+ *   - Returns MOE_ERR_SCRATCH_LIMIT (nothing enqueued) when the layer shape and n_tokens need
+ *     more workspace than the array holds (moe_workspace_size() reports what is needed; the
+ *     shapes of the 3584/64, 2048/512 and 7168/384 layers need at most 4.4 MB at 16 tokens).
+ *   - Every call on one GPU uses that GPU's single array and leaves its contents behind; no
+ *     part of it needs to start at zero (every launch writes what a later one reads).  Calls
+ *     that overlap in time on one GPU (two streams, two threads) race on it: order them on one
+ *     stream.
+ *   - The first call on a device looks up the array's device address (hipGetSymbolAddress)
+ *     and may return MOE_ERR_HIP if that fails. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_decode_layer_noalloc(const moe_desc *desc, const moe_bank *bank,
+                                    const float *w_router, const float *bias, const float *x,
+                                    int32_t n_tokens, float norm_eps, const float *residual,
+                                    float *y, int32_t *topk_ids, float *topk_w, int32_t stages,
+                                    hipStream_t stream);
 
 /* One layer of a decode stack: its expert bank, router [E, H] fp32 and bias [E] (or NULL). */
 typedef struct moe_layer {

@@ -21,6 +21,8 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_UNSUPPORTED = 4
 MOE_ERR_HIP = 5
 MOE_ERR_ALIGNMENT = 6
+MOE_ERR_SCRATCH_LIMIT = 7
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 MOE_GATING_SIGMOID = 0
 MOE_GATING_SOFTMAX = 1
@@ -86,6 +88,8 @@ _SIGNATURES = {
                                 _P, _P, _P, _SZ, _P]),
     "moe_decode_layer": (_I32, [_DESC, _BANK, _P, _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P,
                                 _I32, _P, _SZ, _P]),
+    "moe_decode_layer_noalloc": (_I32, [_DESC, _BANK, _P, _P, _P, _I32, ctypes.c_float, _P, _P,
+                                        _P, _P, _I32, _P]),
 }
 
 _lib = None
@@ -228,6 +232,16 @@ def moe_decode_layer(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual
                                   _ptr(y), _ptr(topk_ids), _ptr(topk_w),
                                   MOE_DECODE_ALL if stages is None else stages, _ptr(ws),
                                   ws_bytes, _stream(stream)))
+
+
+def moe_decode_layer_noalloc(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual, y,
+                             topk_ids, topk_w, stages=None, stream=None):
+    _check("moe_decode_layer_noalloc",
+           lib().moe_decode_layer_noalloc(ctypes.byref(desc), ctypes.byref(bank), _ptr(w_router),
+                                          _ptr(bias), _ptr(x), n_tokens, float(norm_eps),
+                                          _ptr(residual), _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                          MOE_DECODE_ALL if stages is None else stages,
+                                          _stream(stream)))
 
 
 def make_layers(layers):

@@ -10,6 +10,33 @@ namespace moe {
 
 static thread_local int32_t g_last_hip_error = 0;
 
+// Device scratch of moe_decode_layer_noalloc: one array per GPU, resident until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address); it uses the address hipGetSymbolAddress returns for each device.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Address of this device's scratch array (looked up once per device, with it current).
+static hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 int device_cu_count() {
   static int cache[64];
   int dev = 0;
@@ -134,6 +161,9 @@ const char* moe_status_string(int32_t s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported enum value or feature";
     case MOE_ERR_HIP: return "a HIP launch failed (see moe_last_hip_error)";
     case MOE_ERR_ALIGNMENT: return "a pointer or stride violates the alignment contract";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the fixed device array of the allocation-free "
+             "entry point holds (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -271,10 +301,14 @@ moe_status moe_combine(const moe_desc* desc, const float* o, const int32_t* pair
                                         residual, y, stream));
 }
 
-moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const float* w_router,
-                            const float* bias, const float* x, int32_t n_tokens, float norm_eps,
-                            const float* residual, float* y, int32_t* topk_ids, float* topk_w,
-                            int32_t stages, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two fused decode-layer entry points (everything but the workspace).
+moe_status check_decode_layer(const moe_desc* desc, const moe_bank* bank, const float* w_router,
+                              const float* x, int32_t n_tokens, float norm_eps,
+                              const float* residual, float* y, int32_t stages) {
   moe_status st = check_desc(desc);
   if (stages < 1 || stages > MOE_DECODE_ALL) return MOE_ERR_UNSUPPORTED;
   if (st != MOE_OK) return st;
@@ -282,13 +316,20 @@ moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   if (n_tokens > moe::kDecodeMaxTokens) return MOE_ERR_SHAPE;
   if ((st = check_bank(desc, bank)) != MOE_OK) return st;
   if (n_tokens == 0) return MOE_OK;
-  if (!w_router || !x || !y || !ws) return MOE_ERR_NULL;
+  if (!w_router || !x || !y) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(y, 16) ||
-      (residual && !aligned(residual, 16)) || !aligned(ws, 256))
+      (residual && !aligned(residual, 16)))
     return MOE_ERR_ALIGNMENT;
   if (norm_eps != norm_eps) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// The fused decode layer's launches with the workspace at ws (layout decode_layout).
+moe_status run_decode_layer(const moe_desc* desc, const moe_bank* bank, const float* w_router,
+                            const float* bias, const float* x, int32_t n_tokens, float norm_eps,
+                            const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+                            int32_t stages, void* ws, hipStream_t stream) {
   const DecodeLayout L = decode_layout(desc, n_tokens);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   uint8_t* b = static_cast<uint8_t*>(ws);
   moe::DecodeScratch sc;
   sc.logits = reinterpret_cast<float*>(b + L.logits);
@@ -305,6 +346,40 @@ moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
                                              w_router, bias, x, n_tokens, norm_eps, residual, y,
                                              sc, stages, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_layer(const moe_desc* desc, const moe_bank* bank, const float* w_router,
+                            const float* bias, const float* x, int32_t n_tokens, float norm_eps,
+                            const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+                            int32_t stages, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_decode_layer(desc, bank, w_router, x, n_tokens, norm_eps, residual, y,
+                                     stages);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < decode_layout(desc, n_tokens).total) return MOE_ERR_WORKSPACE;
+  return run_decode_layer(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual, y,
+                          topk_ids, topk_w, stages, ws, stream);
+}
+
+moe_status moe_decode_layer_noalloc(const moe_desc* desc, const moe_bank* bank,
+                                    const float* w_router, const float* bias, const float* x,
+                                    int32_t n_tokens, float norm_eps, const float* residual,
+                                    float* y, int32_t* topk_ids, float* topk_w, int32_t stages,
+                                    hipStream_t stream) {
+  moe_status st = check_decode_layer(desc, bank, w_router, x, n_tokens, norm_eps, residual, y,
+                                     stages);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if (decode_layout(desc, n_tokens).total > moe::kNoAllocScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const hipError_t e = moe::scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return run_decode_layer(desc, bank, w_router, bias, x, n_tokens, norm_eps, residual, y,
+                          topk_ids, topk_w, stages, ws, stream);
 }
 
 moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32_t n_layers,
