@@ -1,21 +1,43 @@
 // Prefill path: grouped GEMM of each expert's slot range against its IQ4_NL weights on bf16
-// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
 // Xolotl ("DeepSeek-V4.1-Flash at 27 Tokens/s on One RTX 4090"), section "Prompts: fast, and
 // exact": a prompt chunk runs each layer's experts as one batched multiply.  Red Lite "What we
 // learned", section "3. Speed by release": batched matrix kernels for the experts.
 //
-// Tiles: 128 slot rows x 128 weight rows per workgroup (4 waves, 2 x 2, 64 x 64 each), K in
-// steps of 4 IQ4_NL blocks.  Weight tiles are dequantised once per workgroup into LDS as
-// bf16(d * c[q]) (fp32 product, exact; one RNE rounding); activation tiles are copied into
-// LDS as they are, in natural K order, with coalesced 16-byte loads.  A code byte holds
-// elements j and j+16 of its block, so the dequantisation pairs the lookups of two adjacent
-// code bytes: their low nibbles give elements (2m, 2m+1), their high nibbles (16+2m, 17+2m).
-// For GATE_UP the workgroup's 128 weight rows are 64 gate rows and the 64 matching up rows,
-// arranged so that a lane holds g and u of the same output and applies SwiGLU in registers.
+// Tile: 256 slot rows x 256 weight rows a workgroup, four waves side by side along the weight
+// rows (each wave all 256 slot rows x 64 weight rows: 8 x 2 accumulator tiles of 32 x 32, the
+// 256 accumulator registers of a lane), K in steps of 64 (two IQ4_NL blocks).
 //
-// The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 128) over the
-// experts); a persistent grid walks it, so nothing depends on host-known expert loads.
+//   activations  copied from HBM straight into LDS by the LDS-direct loads of gfx950
+//                (global_load_lds_dwordx4: no registers, no LDS write instructions), one
+//                instruction per 8 whole rows (coalesced), into a ring of 4 stages filled 3
+//                steps ahead; the 16-byte chunks of a row are XOR-swizzled so that every
+//                fragment read is a conflict-free ds_read_b128;
+//   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, 4 steps
+//                ahead (a ring of 4 register slots), and dequantises them there, so every
+//                weight is dequantised once a workgroup and is shared by its 256 slot rows.
+//
+// K order inside a step: the 32 x 32 x 16 instruction takes 8 consecutive k of one operand
+// row per lane, from lane half h = lane / 32.  Instruction i = 0..3 of a step gives lane half
+// h elements 8i .. 8i+7 of block h of the step, for A and B alike (a sum over k may take its
+// terms in any order, so A and B only have to agree), so a lane dequantises one whole block of
+// each of its two weight rows a step.
+//
+// Dequantisation, bf16(d * c[q]) with one RNE rounding of the exact fp32 product: the
+// codebook is symmetric (c[q] = -c[15 - q]), so a block needs the 8 products d * c[q] for
+// q = 0..7 only.  Their bf16 high and low bytes form two 8-byte tables, and one v_perm_b32
+// looks up four elements at a time: magnitude index m = q ^ (q >= 8 ? 8 : 7), then the sign
+// bit flipped for q >= 8.  That is 11 VALU operations per four weights plus 18 per block,
+// no memory access, where a table in LDS costs bank conflicts and LDS bandwidth that the
+// fragment reads need.
+//
+// For GATE_UP a wave's 64 weight rows are 32 gate rows and the 32 matching up rows, so a lane
+// holds g and u of the same output and applies SwiGLU in registers.
+//
+// The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 256) over the
+// experts); the grid is an upper bound on the tile count and a workgroup without a tile
+// exits, so nothing depends on host-known expert loads.
 #include <type_traits>
 
 #include "common.h"
@@ -23,33 +45,279 @@
 
 namespace moe {
 
-constexpr int kBM = 128;               // slot rows per tile
-constexpr int kBN = 128;               // weight rows per tile
-constexpr int kKB = 4;                 // IQ4_NL blocks per K step (128 k)
-constexpr int kLdsStride = kKB * 16 + 4;   // dwords per LDS row (bf16 pairs + pad)
+constexpr int kBM = 256;                 // slot rows per tile
+constexpr int kBN = 256;                 // weight rows per tile
+constexpr int kKS = 64;                  // k per step (2 IQ4_NL blocks)
+constexpr int kStages = 4;               // activation stages in LDS (filled 3 steps ahead)
+constexpr int kBSlots = 4;               // weight-block register slots (filled 4 steps ahead)
 constexpr int kGemmThreads = 256;
-constexpr int kXcds = 8;               // XCDs of an MI355X (each with its own L2)
+constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
+constexpr int kXcds = 8;                 // XCDs of an MI355X (each with its own L2)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+static_assert(kCodebookValues[0] == -kCodebookValues[15] && kCodebookValues[1] == -kCodebookValues[14] &&
+                  kCodebookValues[2] == -kCodebookValues[13] && kCodebookValues[3] == -kCodebookValues[12] &&
+                  kCodebookValues[4] == -kCodebookValues[11] && kCodebookValues[5] == -kCodebookValues[10] &&
+                  kCodebookValues[6] == -kCodebookValues[9] && kCodebookValues[7] == -kCodebookValues[8],
+              "the byte-table dequantisation needs a symmetric codebook");
+static_assert(kStages == kBSlots, "one unrolled loop body per stage and slot");
+
+// Byte tables of one block: entry m (0..7) = bf16(d * c[7 - m]), high bytes in h, low in l.
+struct BlockTab {
+  uint32_t h0, h1, l0, l1;
+};
+
+__device__ __forceinline__ BlockTab block_tab(const RawBlock& r, bool odd) {
+  const float d = block_scale(r, odd);
+  uint32_t p[4];
+#pragma unroll
+  for (int m = 0; m < 8; m += 2)
+    p[m >> 1] = pack_bf16x2(d * (float)kCodebookValues[7 - m], d * (float)kCodebookValues[6 - m]);
+  BlockTab t;
+  t.h0 = __builtin_amdgcn_perm(p[1], p[0], 0x07050301u);
+  t.h1 = __builtin_amdgcn_perm(p[3], p[2], 0x07050301u);
+  t.l0 = __builtin_amdgcn_perm(p[1], p[0], 0x06040200u);
+  t.l1 = __builtin_amdgcn_perm(p[3], p[2], 0x06040200u);
+  return t;
+}
+
+// Four weights from the low (HI = 0) or high (HI = 1) nibbles of one code dword, as two bf16
+// pairs (elements 0,1 and 2,3 of the four).
+template <int HI>
+__device__ __forceinline__ void dequant4(uint32_t cw, const BlockTab& t, uint32_t& o0,
+                                         uint32_t& o1) {
+  uint32_t q, s;                               // q: four 4-bit indices as bytes
+  if (HI) {                                    // s: 0x80 in the bytes whose index is >= 8
+    q = (cw >> 4) & 0x0F0F0F0Fu;
+    s = cw & 0x80808080u;
+  } else {
+    q = cw & 0x0F0F0F0Fu;
+    s = (cw << 4) & 0x80808080u;
+  }
+  const uint32_t m = q ^ (0x07070707u + (s >> 7));           // magnitude index 0..7
+  const uint32_t hb = __builtin_amdgcn_perm(t.h1, t.h0, m) ^ s;
+  const uint32_t lb = __builtin_amdgcn_perm(t.l1, t.l0, m);
+  o0 = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
+}
+
+// B operand of elements 8C .. 8C+7 of a block, from the block's four code dwords.
+template <int C>
+__device__ __forceinline__ bf16x8_t b_frag(const uint32_t (&c)[4], const BlockTab& t) {
+  u32x4_t v;
+  uint32_t a0, a1, a2, a3;
+  dequant4<C / 2>(c[2 * (C & 1)], t, a0, a1);
+  dequant4<C / 2>(c[2 * (C & 1) + 1], t, a2, a3);
+  v[0] = a0; v[1] = a1; v[2] = a2; v[3] = a3;
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// s_waitcnt vmcnt(N): every vector-memory instruction of this wave but the last N issued has
+// completed (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
+// One 18-byte block as five aligned dwords (two load instructions: 16 + 4 bytes).  Blocks
+// with an even index start 4-byte aligned, odd ones 2 bytes past a dword boundary.
+__device__ __forceinline__ RawBlock load_block2(const uint8_t* row, int blk) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + blk * kBlockBytes - (blk & 1) * 2);
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  RawBlock r;
+  r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
+  r.w[4] = p[4];
+  return r;
+}
+
+// One workgroup tile: RG 32-row groups of slot rows hold rows of the tile (the rest of the
+// 256 are past the expert's last slot and are neither multiplied nor stored).
+template <bool GATEUP, int RG>
+__device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restrict__ wmat,
+                                          int64_t row_bytes, const uint16_t* __restrict__ in,
+                                          int64_t row0, int rows_valid, int K, int nt,
+                                          void* __restrict__ out, int H, int F) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform: scalar branches
+  const int c32 = lane & 31, h = lane >> 5;
+  const int NKT = K / kKS;
+
+  // weight rows of this lane: one per 32-column group j of the wave (the columns of a last,
+  // partial DOWN tile past H repeat row H - 1 and are not stored)
+  const uint8_t* brow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int wr;
+    if (GATEUP) {                   // j = 0 gate rows; j = 1 the matching up rows
+      wr = nt * 128 + 32 * wave + c32 + (j ? F : 0);
+    } else {
+      wr = nt * kBN + 64 * wave + 32 * j + c32;
+      if (wr >= H) wr = H - 1;
+    }
+    brow[j] = wmat + (int64_t)wr * row_bytes;
+  }
+
+  // Activations of a step in LDS: row-major, 256 rows x 8 chunks of 16 bytes (8 k each);
+  // chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that read rows
+  // r0 .. r0 + 15 at one chunk cover all 64 banks once.  One copy instruction moves 8 whole
+  // rows (each 128 contiguous bytes of global memory, one cache line): lane l copies chunk
+  // (l & 7) ^ ((row >> 1) & 7) of row 8 n + l / 8 into position l & 7.  Wave w copies the
+  // 8-row groups n = w + 4 s, s < RG, of the 32-row groups that hold rows of the tile (4 RG
+  // groups of 8 rows, RG instructions a wave, n < 4 RG: inside the 32 KB stage); rows past
+  // rows_valid repeat row 0.
+  const uint16_t* tile_in = in + row0 * (int64_t)K;              // uniform
+  uint32_t arow[RG];                        // element offsets from tile_in (< 256 K)
+#pragma unroll
+  for (int s = 0; s < RG; ++s) {
+    const int row = 8 * (wave + 4 * s) + (lane >> 3);
+    arow[s] = (uint32_t)((row < rows_valid ? row : 0) * K + 8 * ((lane & 7) ^ ((row >> 1) & 7)));
+  }
+  // instruction i of a step: lane (c32, h) reads row 32 rg + c32, chunk 4 h + i
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = c32 * 128 + (((4 * h + i) ^ ((c32 >> 1) & 7)) << 4);
+
+  // copies of step kd into stage st (kd clamped to the last step: the same instruction count
+  // every step, which the vmcnt waits below rely on)
+  auto dma_a = [&](int kd, int st) __attribute__((always_inline)) {
+    kd = kd < NKT ? kd : NKT - 1;
+    uint8_t* stage = lds + st * kStageBytes;
+#pragma unroll
+    for (int s = 0; s < RG; ++s)
+    {
+      const int n = wave + 4 * s;         // rows 8 n .. 8 n + 7
+      __builtin_amdgcn_global_load_lds(tile_in + arow[s] + kd * kKS, stage + n * 1024, 16, 0,
+                                       0);
+    }
+  };
+  RawBlock bq[kBSlots][2];
+  auto load_b = [&](int kd, RawBlock (&dst)[2]) __attribute__((always_inline)) {
+    kd = kd < NKT ? kd : NKT - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dst[j] = load_block2(brow[j], 2 * kd + h);
+  };
+
+  f32x16_t acc[RG][2];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[r][j] = f32x16_t{};
+
+  // prologue in the steady state's issue order: B(0) A(0) B(1) A(1) B(2) A(2) B(3)
+  load_b(0, bq[0]);
+  dma_a(0, 0);
+  load_b(1, bq[1]);
+  dma_a(1, 1);
+  load_b(2, bq[2]);
+  dma_a(2, 2);
+  load_b(3, bq[3]);
+
+  // Step kt (U = kt % 4): wait until A(kt) has landed (issued after it: B(kt+1), A(kt+1),
+  // B(kt+2), A(kt+2), B(kt+3) = 3 * 4 + 2 * RG instructions of this wave), barrier, take B(kt)
+  // out of slot U, refill slot U with B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.
+  // Every step issues the same instructions (step indices past the end are clamped), which
+  // the vmcnt counts rely on.
+  constexpr int kOutstanding = 3 * 4 + 2 * RG;
+  auto body = [&](int kt, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    wait_vm<kOutstanding>();
+    lds_barrier();                        // every wave's copies; stage (kt+3) % 4 is free
+    BlockTab tab[2];
+    uint32_t code[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      tab[j] = block_tab(bq[U][j], h != 0);
+      block_codes(bq[U][j], h != 0, code[j]);
+    }
+    dma_a(kt + 3, (U + 3) % kStages);
+    load_b(kt + 4, bq[U]);
+    const uint8_t* stage = lds + U * kStageBytes;
+    // instruction group i: the B fragments of group i + 1 are dequantised while group i's
+    // matrix instructions run; a scheduling barrier between groups keeps the fragment reads
+    // of one group live at a time
+    bf16x8_t bcur[2], bnext[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bcur[j] = b_frag<0>(code[j], tab[j]);
+    auto step = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(ic)::value;
+      if constexpr (I < 3) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bnext[j] = b_frag<I + 1>(code[j], tab[j]);
+      }
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + r * 4096 + aoff[I]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bcur[j], acc[r][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bcur[j] = bnext[j];
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+  };
+  for (int kt = 0; kt < NKT; kt += kStages) {
+    body(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < NKT) body(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < NKT) body(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < NKT) body(kt + 3, std::integral_constant<int, 3>{});
+  }
+  wait_vm<0>();                           // no copy may land in LDS after the tile is done
+
+  // epilogue: lane (c32, h) holds column c32 of each 32 x 32 tile; register e is row
+  // 8 (e / 4) + 4 h + e % 4
+  if (GATEUP) {
+    uint16_t* hout = static_cast<uint16_t*>(out);
+    const int col = nt * 128 + 32 * wave + c32;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m >= rows_valid) continue;
+        const float hv = silu(acc[r][0][e]) * acc[r][1][e];
+        hout[(row0 + m) * (int64_t)F + col] = (uint16_t)(pack_bf16x2(hv, 0.0f) & 0xFFFFu);
+      }
+      __builtin_amdgcn_sched_barrier(0);          // one row group's values live at a time
+    }
+  } else {
+    float* oout = static_cast<float*>(out);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m >= rows_valid) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = nt * kBN + 64 * wave + 32 * j + c32;
+          if (col < H) oout[(row0 + m) * (int64_t)H + col] = acc[r][j][e];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 template <bool GATEUP>
-__global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ in, void* __restrict__ out, int H, int F, int E, int S) {
-  __shared__ __attribute__((aligned(16))) uint32_t sA[kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint32_t sB[kBN * kLdsStride];
-  __shared__ float2 s_tab[256];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[kStages * kStageBytes];
   __shared__ int s_pref[1024];
   __shared__ int s_part[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int q = lane >> 4, c16 = lane & 15;
-
-  s_tab[tid] = make_float2((float)codebook_at(tid & 15), (float)codebook_at(tid >> 4));
 
   // ---- tile prefix over experts: s_pref[e] = sum_{e' <= e} ceil(m_e' / kBM) ----
   const int nbins = E + S;
@@ -81,200 +349,62 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_kernel(
   const int total_m = s_pref[nbins - 1];
 
   const int K = GATEUP ? H : F;
-  const int NB = K >> 5;
-  const int NKT = NB / kKB;
-  const int NT = GATEUP ? F / 64 : H / kBN;
-  const int64_t row_bytes = (int64_t)NB * kBlockBytes;
-  const int64_t mat_off = GATEUP ? 0 : 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
-
-  // XCD-aware walk: workgroup b runs on XCD b % 8 (dispatch is round-robin over the XCDs);
-  // each XCD takes one contiguous range of the tile list, so the workgroups sharing an
-  // activation tile (same M tile, consecutive N tiles) and a weight tile (same expert and N
-  // tile) meet in the same L2.
+  const int NT = GATEUP ? F / 128 : (H + kBN - 1) / kBN;
   const int n_tiles = total_m * NT;
-  const int n_xcd = gridDim.x % kXcds == 0 ? kXcds : 1;
-  const int xcd = blockIdx.x % n_xcd, wix = blockIdx.x / n_xcd, nw = gridDim.x / n_xcd;
-  const int per_xcd = (n_tiles + n_xcd - 1) / n_xcd;
-  const int t_end = min(n_tiles, (xcd + 1) * per_xcd);
-  for (int tile = xcd * per_xcd + wix; tile < t_end; tile += nw) {
-    const int mt = tile / NT, nt = tile % NT;
-    // expert owning M-tile mt: first e with s_pref[e] > mt
-    int lo = 0, hi = nbins - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] > mt) hi = mid; else lo = mid + 1;
-    }
-    const int e = lo;
-    const int m0 = (mt - (e ? s_pref[e - 1] : 0)) * kBM;
-    const int slot0 = offsets[e];
-    const int rows_valid = min(kBM, offsets[e + 1] - slot0 - m0);
-    const uint8_t* wmat = bank + (int64_t)e * stride + mat_off;
-
-    // weight rows this thread dequantises (2 units: LDS row n, block kk)
-    const uint8_t* brow[2];
-    int bn[2], bk[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + kGemmThreads * i;
-      const int n = v >> 2;
-      bn[i] = n;
-      bk[i] = v & 3;
-      int wr;
-      if (GATEUP) {
-        const int half = n >> 6, rr = n & 63;
-        wr = (rr < 32) ? (nt * 64 + 32 * half + rr) : (F + nt * 64 + 32 * half + rr - 32);
-      } else {
-        wr = nt * kBN + n;
-      }
-      brow[i] = wmat + (int64_t)wr * row_bytes;
-    }
-    // activation chunks this thread stages (8 units of 16 B: row u >> 4, chunk u & 15).  Rows
-    // past the tile's end copy row 0 instead (their output rows are never stored): unconditional
-    // loads keep the compiler's load counting exact, so the loads stay in flight
-    const uint16_t* arow[8];
-    int aoff[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int u = tid + kGemmThreads * i;
-      const int r = u >> 4, c = u & 15;
-      arow[i] = in + (int64_t)(slot0 + m0 + (r < rows_valid ? r : 0)) * K + 8 * c;
-      aoff[i] = r * kLdsStride + 4 * c;
-    }
-
-    // 16-row groups of this wave's 64 rows that hold slot rows of the tile
-    const int wgroups = min(4, max(0, (rows_valid - wm * 64 + 15) >> 4));
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // K loop, software-pipelined: the global loads of step kt+1 are issued as soon as the
-    // registers of step kt are in LDS (activations first, then weights) and stay in flight
-    // while the MFMAs of step kt run; barriers order LDS only.
-    u32x4_t ga[4][2];   // (a native vector type: whole-struct copies would go through scratch)
-    RawBlock gb[2];
-    auto gload_a = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        ga[i >> 1][i & 1] = *reinterpret_cast<const u32x4_t*>(arow[i] + kt * kKB * 32);
-    };
-    auto gload_b = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) gb[i] = load_block(brow[i], kt * kKB + bk[i]);
-    };
-    gload_a(0);
-    gload_b(0);
-    for (int kt = 0; kt < NKT; ++kt) {
-      lds_barrier();     // every wave is done reading the previous step's tiles
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4_t*>(&sA[aoff[i]]) = ga[i >> 1][i & 1];
-      if (kt + 1 < NKT) gload_a(kt + 1);
-      // B -> LDS: dequantise to bf16(d * c) in natural K order: dword m < 8 holds elements
-      // (2m, 2m+1), the low nibbles of code bytes 2m and 2m+1; dword 8+m their high nibbles
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bool odd = (bk[i] & 1) != 0;
-        const float dsc = block_scale(gb[i], odd);
-        uint32_t cw[4];
-        block_codes(gb[i], odd, cw);
-        uint32_t o[16];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float2 ta = s_tab[(cw[m >> 1] >> (16 * (m & 1))) & 0xFFu];
-          const float2 tb = s_tab[(cw[m >> 1] >> (16 * (m & 1) + 8)) & 0xFFu];
-          o[m] = pack_bf16x2(ta.x * dsc, tb.x * dsc);
-          o[8 + m] = pack_bf16x2(ta.y * dsc, tb.y * dsc);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&sB[bn[i] * kLdsStride + bk[i] * 16]);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-        dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
-      }
-      if (kt + 1 < NKT) gload_b(kt + 1);
-      lds_barrier();
-      // the MFMA phase runs at raised wave priority, so that on a SIMD shared with a wave of
-      // the other workgroup the matrix core is fed first and the staging fills the gaps
-      __builtin_amdgcn_s_setprio(1);
-      // only the 16-row groups of this wave that hold slot rows of the tile are multiplied
-      // (a wave whose 64 rows are all past the tile's end has nothing to compute)
-      auto mma = [&](auto gc) __attribute__((always_inline)) {
-        constexpr int G = decltype(gc)::value;
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-          bf16x8_t af[G], bfr[4];
-#pragma unroll
-          for (int i = 0; i < G; ++i)
-            af[i] = *reinterpret_cast<const bf16x8_t*>(
-                &sA[(wm * 64 + 16 * i + c16) * kLdsStride + kb * 16 + 4 * q]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-                &sB[(wn * 64 + 16 * j + c16) * kLdsStride + kb * 16 + 4 * q]);
-#pragma unroll
-          for (int i = 0; i < G; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-      };
-      switch (wgroups) {
-        case 0: break;
-        case 1: mma(std::integral_constant<int, 1>{}); break;
-        case 2: mma(std::integral_constant<int, 2>{}); break;
-        case 3: mma(std::integral_constant<int, 3>{}); break;
-        default: mma(std::integral_constant<int, 4>{}); break;
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-
-    // epilogue: lane holds column c16 of each 16x16 sub-tile, rows 4q .. 4q+3
-    if (GATEUP) {
-      uint16_t* hout = static_cast<uint16_t*>(out);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = wm * 64 + 16 * i + 4 * q + r;
-          if (m >= rows_valid) continue;
-          const int64_t orow = (int64_t)(slot0 + m0 + m) * F;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * 64 + 32 * wn + 16 * j + c16;
-            const float h = silu(acc[i][j][r]) * acc[i][j + 2][r];
-            hout[orow + col] = (uint16_t)(pack_bf16x2(h, 0.0f) & 0xFFFFu);
-          }
-        }
-    } else {
-      float* oout = static_cast<float*>(out);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = wm * 64 + 16 * i + 4 * q + r;
-          if (m >= rows_valid) continue;
-          const int64_t orow = (int64_t)(slot0 + m0 + m) * H;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) oout[orow + nt * kBN + wn * 64 + 16 * j + c16] = acc[i][j][r];
-        }
-    }
+  // XCD-aware order: workgroup b runs on XCD b % 8 (dispatch is round-robin over the XCDs);
+  // each XCD walks one contiguous range of the tile list, so the workgroups that share an
+  // activation panel (same M tile, consecutive N tiles) or a weight tile (same expert and N
+  // tile) meet in the same L2
+  const int xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
+  const int per_xcd = (n_tiles + kXcds - 1) / kXcds;
+  const int tile = xcd * per_xcd + idx;
+  if (idx >= per_xcd || tile >= n_tiles) return;
+  const int mt = tile / NT, nt = tile % NT;
+  // expert owning M tile mt: first e with s_pref[e] > mt
+  int lo = 0, hi = nbins - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] > mt) hi = mid; else lo = mid + 1;
   }
+  const int e = lo;
+  const int m0 = (mt - (e ? s_pref[e - 1] : 0)) * kBM;
+  const int64_t row0 = (int64_t)offsets[e] + m0;
+  const int rows_valid = min(kBM, offsets[e + 1] - offsets[e] - m0);
+  const int64_t row_bytes = (int64_t)(K >> 5) * kBlockBytes;
+  const int64_t mat_off = GATEUP ? 0 : 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+  const uint8_t* wmat = bank + (int64_t)e * stride + mat_off;
+  const int rg = (rows_valid + 31) >> 5;
+
+#define TILE(N) \
+  case N: gemm_tile<GATEUP, N>(s_a, wmat, row_bytes, in, row0, rows_valid, K, nt, out, H, F); break;
+  switch (rg) {
+    TILE(1) TILE(2) TILE(3) TILE(4) TILE(5) TILE(6) TILE(7) TILE(8)
+    default: break;
+  }
+#undef TILE
 }
 
 hipError_t launch_gemm(const Shape& sh, int stage, const uint8_t* bank, int64_t stride,
                        const int32_t* offsets, const void* in, void* out, int T,
                        hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int grid = device_cu_count() * 2;
+  // upper bound on the tiles: every expert with slots adds at most one partial M tile
+  const int64_t rows = (int64_t)T * (sh.k + sh.S);
+  const int64_t bins = std::min<int64_t>(sh.E + sh.S, rows);
+  const int64_t mtiles = (rows + kBM - 1) / kBM + bins;
+  const int NT = stage == 0 ? sh.F / 128 : (sh.H + kBN - 1) / kBN;
+  const int64_t tiles = mtiles * NT;
+  // rounded up to whole XCD rows: tile ranges are split evenly over the eight XCDs
+  const int64_t grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (stage == 0)
-    hipLaunchKernelGGL(gemm_kernel<true>, dim3(grid), dim3(kGemmThreads), 0, s, bank, stride,
-                       offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F, sh.E, sh.S);
+    hipLaunchKernelGGL(gemm_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, bank,
+                       stride, offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F, sh.E,
+                       sh.S);
   else
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3(grid), dim3(kGemmThreads), 0, s, bank, stride,
-                       offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F, sh.E, sh.S);
+    hipLaunchKernelGGL(gemm_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+                       bank, stride, offsets, static_cast<const uint16_t*>(in), out, sh.H, sh.F,
+                       sh.E, sh.S);
   return hipGetLastError();
 }
 
