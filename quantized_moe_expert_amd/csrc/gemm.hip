@@ -5,9 +5,11 @@
 // exact": a prompt chunk runs each layer's experts as one batched multiply.  Red Lite "What we
 // learned", section "3. Speed by release": batched matrix kernels for the experts.
 //
-// Tile: 256 slot rows x 256 weight rows a workgroup, four waves side by side along the weight
-// rows (each wave all 256 slot rows x 64 weight rows: 8 x 2 accumulator tiles of 32 x 32, the
-// 256 accumulator registers of a lane), K in steps of 64 (two IQ4_NL blocks).
+// Tile: 256 slot rows x 256 weight rows a workgroup, eight waves side by side along the weight
+// rows (each wave all 256 slot rows x 32 weight rows: 8 accumulator tiles of 32 x 32, 128
+// accumulator registers a lane), two waves a SIMD so that one wave's waits for LDS, memory and
+// the barrier are covered by the other's matrix instructions; K in steps of 64 (two IQ4_NL
+// blocks).
 //
 //   activations  copied from HBM straight into LDS by the LDS-direct loads of gfx950
 //                (global_load_lds_dwordx4: no registers, no LDS write instructions), one
@@ -15,14 +17,15 @@
 //                steps ahead; the 16-byte chunks of a row are XOR-swizzled so that every
 //                fragment read is a conflict-free ds_read_b128;
 //   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, 4 steps
-//                ahead (a ring of 4 register slots), and dequantises them there, so every
-//                weight is dequantised once a workgroup and is shared by its 256 slot rows.
+//                ahead (a ring of 4 register slots), and dequantises them there; each weight
+//                row belongs to one wave, so every weight is dequantised once a workgroup and
+//                is shared by its 256 slot rows.
 //
 // K order inside a step: the 32 x 32 x 16 instruction takes 8 consecutive k of one operand
 // row per lane, from lane half h = lane / 32.  Instruction i = 0..3 of a step gives lane half
 // h elements 8i .. 8i+7 of block h of the step, for A and B alike (a sum over k may take its
 // terms in any order, so A and B only have to agree), so a lane dequantises one whole block of
-// each of its two weight rows a step.
+// its weight row a step.
 //
 // Dequantisation, bf16(d * c[q]) with one RNE rounding of the exact fp32 product: the
 // codebook is symmetric (c[q] = -c[15 - q]), so a block needs the 8 products d * c[q] for
@@ -32,8 +35,9 @@
 // no memory access, where a table in LDS costs bank conflicts and LDS bandwidth that the
 // fragment reads need.
 //
-// For GATE_UP a wave's 64 weight rows are 32 gate rows and the 32 matching up rows, so a lane
-// holds g and u of the same output and applies SwiGLU in registers.
+// For GATE_UP a wave's 32 weight rows are 16 gate rows (lanes c < 16 of a half) and the 16
+// matching up rows (lanes c + 16), so u reaches the lane holding g by one lane swap and SwiGLU
+// is applied in registers.
 //
 // The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 256) over the
 // experts); the grid is an upper bound on the tile count and a workgroup without a tile
@@ -50,7 +54,8 @@ constexpr int kBN = 256;                 // weight rows per tile
 constexpr int kKS = 64;                  // k per step (2 IQ4_NL blocks)
 constexpr int kStages = 4;               // activation stages in LDS (filled 3 steps ahead)
 constexpr int kBSlots = 4;               // weight-block register slots (filled 4 steps ahead)
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;
+constexpr int kCopyWaves = 4;            // waves that issue the activation copies
 constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
 constexpr int kXcds = 8;                 // XCDs of an MI355X (each with its own L2)
 
@@ -147,20 +152,16 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   const int c32 = lane & 31, h = lane >> 5;
   const int NKT = K / kKS;
 
-  // weight rows of this lane: one per 32-column group j of the wave (the columns of a last,
-  // partial DOWN tile past H repeat row H - 1 and are not stored)
-  const uint8_t* brow[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int wr;
-    if (GATEUP) {                   // j = 0 gate rows; j = 1 the matching up rows
-      wr = nt * 128 + 32 * wave + c32 + (j ? F : 0);
-    } else {
-      wr = nt * kBN + 64 * wave + 32 * j + c32;
-      if (wr >= H) wr = H - 1;
-    }
-    brow[j] = wmat + (int64_t)wr * row_bytes;
+  // the weight row of this lane: column c32 of the wave's 32 (the columns of a last, partial
+  // DOWN tile past H repeat row H - 1 and are not stored)
+  int wr;
+  if (GATEUP) {                     // c32 < 16: gate rows; c32 >= 16: the matching up rows
+    wr = nt * 128 + 16 * wave + (c32 & 15) + (c32 >= 16 ? F : 0);
+  } else {
+    wr = nt * kBN + 32 * wave + c32;
+    if (wr >= H) wr = H - 1;
   }
+  const uint8_t* brow = wmat + (int64_t)wr * row_bytes;
 
   // Activations of a step in LDS: row-major, 256 rows x 8 chunks of 16 bytes (8 k each);
   // chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that read rows
@@ -168,13 +169,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   // rows (each 128 contiguous bytes of global memory, one cache line): lane l copies chunk
   // (l & 7) ^ ((row >> 1) & 7) of row 8 n + l / 8 into position l & 7.  Wave w copies the
   // 8-row groups n = w + 4 s, s < RG, of the 32-row groups that hold rows of the tile (4 RG
-  // groups of 8 rows, RG instructions a wave, n < 4 RG: inside the 32 KB stage); rows past
-  // rows_valid repeat row 0.
+  // groups of 8 rows, RG instructions each of waves 0..3, n < 4 RG: inside the 32 KB stage);
+  // rows past rows_valid repeat row 0.
   const uint16_t* tile_in = in + row0 * (int64_t)K;              // uniform
   uint32_t arow[RG];                        // element offsets from tile_in (< 256 K)
 #pragma unroll
   for (int s = 0; s < RG; ++s) {
-    const int row = 8 * (wave + 4 * s) + (lane >> 3);
+    const int row = 8 * ((wave & 3) + 4 * s) + (lane >> 3);
     arow[s] = (uint32_t)((row < rows_valid ? row : 0) * K + 8 * ((lane & 7) ^ ((row >> 1) & 7)));
   }
   // instruction i of a step: lane (c32, h) reads row 32 rg + c32, chunk 4 h + i
@@ -185,6 +186,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   // copies of step kd into stage st (kd clamped to the last step: the same instruction count
   // every step, which the vmcnt waits below rely on)
   auto dma_a = [&](int kd, int st) __attribute__((always_inline)) {
+    if (wave >= kCopyWaves) return;
     kd = kd < NKT ? kd : NKT - 1;
     uint8_t* stage = lds + st * kStageBytes;
 #pragma unroll
@@ -195,18 +197,15 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
                                        0);
     }
   };
-  RawBlock bq[kBSlots][2];
-  auto load_b = [&](int kd, RawBlock (&dst)[2]) __attribute__((always_inline)) {
+  RawBlock bq[kBSlots];
+  auto load_b = [&](int kd, RawBlock& dst) __attribute__((always_inline)) {
     kd = kd < NKT ? kd : NKT - 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dst[j] = load_block2(brow[j], 2 * kd + h);
+    dst = load_block2(brow, 2 * kd + h);
   };
 
-  f32x16_t acc[RG][2];
+  f32x16_t acc[RG];
 #pragma unroll
-  for (int r = 0; r < RG; ++r)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[r][j] = f32x16_t{};
+  for (int r = 0; r < RG; ++r) acc[r] = f32x16_t{};
 
   // prologue in the steady state's issue order: B(0) A(0) B(1) A(1) B(2) A(2) B(3)
   load_b(0, bq[0]);
@@ -217,48 +216,36 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   dma_a(2, 2);
   load_b(3, bq[3]);
 
-  // Step kt (U = kt % 4): wait until A(kt) has landed (issued after it: B(kt+1), A(kt+1),
-  // B(kt+2), A(kt+2), B(kt+3) = 3 * 4 + 2 * RG instructions of this wave), barrier, take B(kt)
-  // out of slot U, refill slot U with B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.
-  // Every step issues the same instructions (step indices past the end are clamped), which
-  // the vmcnt counts rely on.
-  constexpr int kOutstanding = 3 * 4 + 2 * RG;
+  // Step kt (U = kt % 4): wait until A(kt) has landed (a copying wave issued after it: B(kt+1),
+  // A(kt+1), B(kt+2), A(kt+2), B(kt+3) = 3 * 2 + 2 * RG instructions), barrier, take B(kt) out
+  // of slot U, refill slot U with B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.  Every
+  // step issues the same instructions (step indices past the end are clamped), which the vmcnt
+  // count relies on; the waves that copy nothing wait for their own blocks only.
+  constexpr int kOutstanding = 3 * 2 + 2 * RG;
   auto body = [&](int kt, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
-    wait_vm<kOutstanding>();
+    if (wave < kCopyWaves) wait_vm<kOutstanding>();
     lds_barrier();                        // every wave's copies; stage (kt+3) % 4 is free
-    BlockTab tab[2];
-    uint32_t code[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      tab[j] = block_tab(bq[U][j], h != 0);
-      block_codes(bq[U][j], h != 0, code[j]);
-    }
+    const BlockTab tab = block_tab(bq[U], h != 0);
+    uint32_t code[4];
+    block_codes(bq[U], h != 0, code);
     dma_a(kt + 3, (U + 3) % kStages);
     load_b(kt + 4, bq[U]);
     const uint8_t* stage = lds + U * kStageBytes;
-    // instruction group i: the B fragments of group i + 1 are dequantised while group i's
+    // instruction group i: the B fragment of group i + 1 is dequantised while group i's
     // matrix instructions run; a scheduling barrier between groups keeps the fragment reads
     // of one group live at a time
-    bf16x8_t bcur[2], bnext[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) bcur[j] = b_frag<0>(code[j], tab[j]);
+    bf16x8_t bcur = b_frag<0>(code, tab), bnext;
     auto step = [&](auto ic) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value;
-      if constexpr (I < 3) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bnext[j] = b_frag<I + 1>(code[j], tab[j]);
-      }
+      if constexpr (I < 3) bnext = b_frag<I + 1>(code, tab);
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
         const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + r * 4096 + aoff[I]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bcur[j], acc[r][j], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bcur, acc[r], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bcur[j] = bnext[j];
+      bcur = bnext;
     };
     step(std::integral_constant<int, 0>{});
     step(std::integral_constant<int, 1>{});
@@ -277,31 +264,30 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   // 8 (e / 4) + 4 h + e % 4
   if (GATEUP) {
     uint16_t* hout = static_cast<uint16_t*>(out);
-    const int col = nt * 128 + 32 * wave + c32;
+    const int col = nt * 128 + 16 * wave + (c32 & 15);
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
+        const float g = acc[r][e];
+        const float u = __shfl_xor(g, 16, 64);         // the up value of the same output
         const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m >= rows_valid) continue;
-        const float hv = silu(acc[r][0][e]) * acc[r][1][e];
+        if (c32 >= 16 || m >= rows_valid) continue;
+        const float hv = silu(g) * u;
         hout[(row0 + m) * (int64_t)F + col] = (uint16_t)(pack_bf16x2(hv, 0.0f) & 0xFFFFu);
       }
       __builtin_amdgcn_sched_barrier(0);          // one row group's values live at a time
     }
   } else {
     float* oout = static_cast<float*>(out);
+    const int col = nt * kBN + 32 * wave + c32;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m >= rows_valid) continue;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * kBN + 64 * wave + 32 * j + c32;
-          if (col < H) oout[(row0 + m) * (int64_t)H + col] = acc[r][j][e];
-        }
+        if (m >= rows_valid || col >= H) continue;
+        oout[(row0 + m) * (int64_t)H + col] = acc[r][e];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -314,7 +300,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(
     const uint16_t* __restrict__ in, void* __restrict__ out, int H, int F, int E, int S) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_a[kStages * kStageBytes];
   __shared__ int s_pref[1024];
-  __shared__ int s_part[4];
+  __shared__ int s_part[kGemmThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
