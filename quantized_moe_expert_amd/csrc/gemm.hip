@@ -14,8 +14,10 @@
 //   activations  copied from HBM straight into LDS by the LDS-direct loads of gfx950
 //                (global_load_lds_dwordx4: no registers, no LDS write instructions), one
 //                instruction per 8 whole rows (coalesced), into a ring of 4 stages filled 3
-//                steps ahead; the 16-byte chunks of a row are XOR-swizzled so that every
-//                fragment read is a conflict-free ds_read_b128;
+//                steps ahead, the copies of a step spread evenly over the eight waves; the
+//                16-byte chunks of a row are XOR-swizzled so that every fragment read is a
+//                conflict-free ds_read_b128, and the reads run three matrix instructions
+//                ahead of their use;
 //   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, 4 steps
 //                ahead (a ring of 4 register slots), and dequantises them there; each weight
 //                row belongs to one wave, so every weight is dequantised once a workgroup and
@@ -43,6 +45,7 @@
 // experts); the grid is an upper bound on the tile count and a workgroup without a tile
 // exits, so nothing depends on host-known expert loads.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -55,9 +58,9 @@ constexpr int kKS = 64;                  // k per step (2 IQ4_NL blocks)
 constexpr int kStages = 4;               // activation stages in LDS (filled 3 steps ahead)
 constexpr int kBSlots = 4;               // weight-block register slots (filled 4 steps ahead)
 constexpr int kGemmThreads = 512;
-constexpr int kCopyWaves = 4;            // waves that issue the activation copies
 constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
-constexpr int kXcds = 8;                 // XCDs of an MI355X (each with its own L2)
+constexpr int kXcds = 8;                  // XCDs of an MI355X (each with its own L2)
+constexpr int kWin = 4;                   // A-fragment reads in flight, plus one
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -129,6 +132,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N - 1>{}), in order
+template <int N, typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// s_waitcnt lgkmcnt(N): every LDS instruction of this wave but the last N issued has completed.
+// The compiler counts the activation copies into LDS as outstanding on both counters and, while
+// one is in flight, turns every wait it adds itself into a full drain; a wait written here that
+// already covers the dependency leaves it nothing to add.
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
+}
+
 // One 18-byte block as five aligned dwords (two load instructions: 16 + 4 bytes).  Blocks
 // with an even index start 4-byte aligned, odd ones 2 bytes past a dword boundary.
 __device__ __forceinline__ RawBlock load_block2(const uint8_t* row, int blk) {
@@ -143,7 +166,8 @@ __device__ __forceinline__ RawBlock load_block2(const uint8_t* row, int blk) {
 // One workgroup tile: RG 32-row groups of slot rows hold rows of the tile (the rest of the
 // 256 are past the expert's last slot and are neither multiplied nor stored).
 template <bool GATEUP, int RG>
-__device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restrict__ wmat,
+__device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t* lds2,
+                                          uint8_t* lds3, const uint8_t* __restrict__ wmat,
                                           int64_t row_bytes, const uint16_t* __restrict__ in,
                                           int64_t row0, int rows_valid, int K, int nt,
                                           void* __restrict__ out, int H, int F) {
@@ -167,15 +191,21 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
   // chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that read rows
   // r0 .. r0 + 15 at one chunk cover all 64 banks once.  One copy instruction moves 8 whole
   // rows (each 128 contiguous bytes of global memory, one cache line): lane l copies chunk
-  // (l & 7) ^ ((row >> 1) & 7) of row 8 n + l / 8 into position l & 7.  Wave w copies the
-  // 8-row groups n = w + 4 s, s < RG, of the 32-row groups that hold rows of the tile (4 RG
-  // groups of 8 rows, RG instructions each of waves 0..3, n < 4 RG: inside the 32 KB stage);
-  // rows past rows_valid repeat row 0.
+  // (l & 7) ^ ((row >> 1) & 7) of row 8 n + l / 8 into position l & 7.  The tile's rows
+  // holding slot rows are 4 RG groups of 8; wave w copies groups n = w + 8 s, s < RG / 2, and
+  // when RG is odd one more, n = (w & 3) + 8 (RG / 2) -- waves w and w + 4 then copy the same
+  // group, the same bytes to the same place.  Every wave issues the same number of copies
+  // (NA), so the vector-memory counts of all waves agree and no branch surrounds a load (a
+  // branch around loads makes the compiler drain every outstanding load where the paths
+  // meet).  n < 4 RG: inside the 32 KB stage.  Rows past rows_valid repeat row 0.
+  constexpr int NA = (RG + 1) / 2;
   const uint16_t* tile_in = in + row0 * (int64_t)K;              // uniform
-  uint32_t arow[RG];                        // element offsets from tile_in (< 256 K)
+  uint32_t arow[NA];                        // element offsets from tile_in (< 256 K)
+  int an[NA];
 #pragma unroll
-  for (int s = 0; s < RG; ++s) {
-    const int row = 8 * ((wave & 3) + 4 * s) + (lane >> 3);
+  for (int s = 0; s < NA; ++s) {
+    an[s] = s < RG / 2 ? wave + 8 * s : (wave & 3) + 8 * s;
+    const int row = 8 * an[s] + (lane >> 3);
     arow[s] = (uint32_t)((row < rows_valid ? row : 0) * K + 8 * ((lane & 7) ^ ((row >> 1) & 7)));
   }
   // instruction i of a step: lane (c32, h) reads row 32 rg + c32, chunk 4 h + i
@@ -183,19 +213,20 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff[i] = c32 * 128 + (((4 * h + i) ^ ((c32 >> 1) & 7)) << 4);
 
+  // The four stages are four LDS arrays, not one: the compiler then knows that reads of one
+  // stage do not alias copies into another and adds no wait of its own between them.
+  auto stage_of = [&](int st) __attribute__((always_inline)) {
+    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
+  };
   // copies of step kd into stage st (kd clamped to the last step: the same instruction count
   // every step, which the vmcnt waits below rely on)
   auto dma_a = [&](int kd, int st) __attribute__((always_inline)) {
-    if (wave >= kCopyWaves) return;
     kd = kd < NKT ? kd : NKT - 1;
-    uint8_t* stage = lds + st * kStageBytes;
+    uint8_t* stage = stage_of(st);
 #pragma unroll
-    for (int s = 0; s < RG; ++s)
-    {
-      const int n = wave + 4 * s;         // rows 8 n .. 8 n + 7
-      __builtin_amdgcn_global_load_lds(tile_in + arow[s] + kd * kKS, stage + n * 1024, 16, 0,
-                                       0);
-    }
+    for (int s = 0; s < NA; ++s)          // rows 8 n .. 8 n + 7
+      __builtin_amdgcn_global_load_lds(tile_in + arow[s] + kd * kKS, stage + an[s] * 1024, 16,
+                                       0, 0);
   };
   RawBlock bq[kBSlots];
   auto load_b = [&](int kd, RawBlock& dst) __attribute__((always_inline)) {
@@ -207,57 +238,102 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds, const uint8_t* __restric
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = f32x16_t{};
 
-  // prologue in the steady state's issue order: B(0) A(0) B(1) A(1) B(2) A(2) B(3)
+  // Issue order, pinned by scheduling barriers (the vmcnt count below depends on it): B(0) B(1)
+  // A(0), then B(j + 2) A(j + 1) in turn -- the prologue up to A(2), each step kt one pair
+  // B(kt + 4) A(kt + 3).
   load_b(0, bq[0]);
-  dma_a(0, 0);
   load_b(1, bq[1]);
-  dma_a(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(2, bq[2]);
-  dma_a(2, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(3, bq[3]);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_a(2, 2);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Step kt (U = kt % 4): wait until A(kt) has landed (a copying wave issued after it: B(kt+1),
-  // A(kt+1), B(kt+2), A(kt+2), B(kt+3) = 3 * 2 + 2 * RG instructions), barrier, take B(kt) out
-  // of slot U, refill slot U with B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.  Every
-  // step issues the same instructions (step indices past the end are clamped), which the vmcnt
-  // count relies on; the waves that copy nothing wait for their own blocks only.
-  constexpr int kOutstanding = 3 * 2 + 2 * RG;
+  // Step kt (U = kt % 4): wait until A(kt) has landed (issued after it: B(kt+2), A(kt+1),
+  // B(kt+3), A(kt+2) = 2 * 2 + 2 * NA instructions of this wave; B(kt) came before it), then
+  // a barrier: every wave's copies of A(kt) are in, and every wave has used its reads of
+  // stage (kt+3) % 4 from step kt - 1.  The barrier carries no memory fence: a workgroup
+  // release fence makes the compiler wait for every copy still in flight (vmcnt(0)), which
+  // would undo the prefetch; the explicit waits order the copies, the lgkmcnt(0) this wave's
+  // LDS reads, and the memory clobber keeps the compiler from moving LDS accesses across.
+  // The scheduling barrier after it keeps the first uses of B(kt) below the wait, where the
+  // compiler has nothing left to wait for.  Then take B(kt) out of slot U, refill slot U with
+  // B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.  Every step issues the same
+  // instructions (step indices past the end are clamped), which the vmcnt count relies on.
+  constexpr int kOutstanding = 2 * 2 + 2 * NA;
   auto body = [&](int kt, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
-    if (wave < kCopyWaves) wait_vm<kOutstanding>();
-    lds_barrier();                        // every wave's copies; stage (kt+3) % 4 is free
+    wait_vm<kOutstanding>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     const BlockTab tab = block_tab(bq[U], h != 0);
     uint32_t code[4];
     block_codes(bq[U], h != 0, code);
-    dma_a(kt + 3, (U + 3) % kStages);
     load_b(kt + 4, bq[U]);
-    const uint8_t* stage = lds + U * kStageBytes;
-    // instruction group i: the B fragment of group i + 1 is dequantised while group i's
-    // matrix instructions run; a scheduling barrier between groups keeps the fragment reads
-    // of one group live at a time
-    bf16x8_t bcur = b_frag<0>(code, tab), bnext;
-    auto step = [&](auto ic) __attribute__((always_inline)) {
-      constexpr int I = decltype(ic)::value;
-      if constexpr (I < 3) bnext = b_frag<I + 1>(code, tab);
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(stage + r * 4096 + aoff[I]);
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bcur, acc[r], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(kt + 3, (U + 3) % kStages);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* stage = stage_of(U);
+    // Matrix instruction j of the step (j < 4 RG): group I = j / RG (k 16 I .. 16 I + 15),
+    // row group r = j % RG.  Its A fragment is read kWin - 1 instructions ahead, so that
+    // kWin - 1 LDS reads are in flight behind every matrix instruction instead of one read
+    // waited for before each; the B fragment of group I + 1 is dequantised, one half at a
+    // time, beside the first two instructions of group I.  A scheduling barrier after each
+    // instruction keeps this order (left alone, the compiler issues a read and waits for it
+    // before each one).
+    constexpr int NJ = 4 * RG;
+    bf16x8_t af[kWin];
+    bf16x8_t bf[2];
+    uint32_t bn[4];
+    auto read_a = [&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      af[J % kWin] = *reinterpret_cast<const bf16x8_t*>(stage + (J % RG) * 4096 + aoff[J / RG]);
+    };
+    static_for<(kWin - 1 < NJ ? kWin - 1 : NJ)>([&](auto jc) { read_a(jc); });
+    bf[0] = b_frag<0>(code, tab);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NJ>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value, I = J / RG, R = J % RG;
+      // fragment J's read is done once at most the reads issued after it (kWin - 2 of them, or
+      // to the step's end) are in flight; the read of fragment J + kWin - 1 goes out after
+      wait_lgkm<(kWin - 2 < NJ - 1 - J ? kWin - 2 : NJ - 1 - J)>();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (J + kWin - 1 < NJ) read_a(std::integral_constant<int, J + kWin - 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      acc[R] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[J % kWin], bf[I & 1], acc[R], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (I < 3) {
+        constexpr int C = I + 1;                // the next group's fragment, in two halves
+        if constexpr (R == 0)
+          dequant4<C / 2>(code[2 * (C & 1)], tab, bn[0], bn[1]);
+        if constexpr (R == (RG > 1 ? 1 : 0)) {
+          dequant4<C / 2>(code[2 * (C & 1) + 1], tab, bn[2], bn[3]);
+          u32x4_t v;
+          v[0] = bn[0]; v[1] = bn[1]; v[2] = bn[2]; v[3] = bn[3];
+          bf[C & 1] = __builtin_bit_cast(bf16x8_t, v);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      bcur = bnext;
-    };
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    step(std::integral_constant<int, 3>{});
+    });
   };
-  for (int kt = 0; kt < NKT; kt += kStages) {
+  // whole groups of four steps in the loop, the remainder after it: no conditional step inside
+  // the loop, whose paths would again meet with different outstanding loads
+  int kt = 0;
+  for (; kt + kStages <= NKT; kt += kStages) {
     body(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < NKT) body(kt + 1, std::integral_constant<int, 1>{});
-    if (kt + 2 < NKT) body(kt + 2, std::integral_constant<int, 2>{});
-    if (kt + 3 < NKT) body(kt + 3, std::integral_constant<int, 3>{});
+    body(kt + 1, std::integral_constant<int, 1>{});
+    body(kt + 2, std::integral_constant<int, 2>{});
+    body(kt + 3, std::integral_constant<int, 3>{});
   }
+  if (kt < NKT) body(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < NKT) body(kt + 1, std::integral_constant<int, 1>{});
+  if (kt + 2 < NKT) body(kt + 2, std::integral_constant<int, 2>{});
   wait_vm<0>();                           // no copy may land in LDS after the tile is done
 
   // epilogue: lane (c32, h) holds column c32 of each 32 x 32 tile; register e is row
@@ -298,7 +374,10 @@ template <bool GATEUP>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ in, void* __restrict__ out, int H, int F, int E, int S) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a3[kStageBytes];
   __shared__ int s_pref[1024];
   __shared__ int s_part[kGemmThreads / 64];
 
@@ -362,7 +441,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(
   const int rg = (rows_valid + 31) >> 5;
 
 #define TILE(N) \
-  case N: gemm_tile<GATEUP, N>(s_a, wmat, row_bytes, in, row0, rows_valid, K, nt, out, H, F); break;
+  case N: gemm_tile<GATEUP, N>(s_a0, s_a1, s_a2, s_a3, wmat, row_bytes, in, row0, rows_valid, K, nt, out, H, F); break;
   switch (rg) {
     TILE(1) TILE(2) TILE(3) TILE(4) TILE(5) TILE(6) TILE(7) TILE(8)
     default: break;
