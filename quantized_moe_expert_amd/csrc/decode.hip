@@ -9,10 +9,11 @@
 //   router  : one workgroup per EPW experts; logits of all T tokens from one pass over W_r,
 //             together with sum(x^2) per token (the RMSNorm scale is applied to the dot
 //             product: (W_r x) / rms(x) = W_r (x / rms(x))).
-//   gate/up : every workgroup redoes the top-k and the route histogram of the T tokens
-//             (a few microseconds of LDS work, no cross-workgroup state), picks its expert
-//             (the blockIdx.y-th active one), streams its rows and writes h in slot order;
-//             workgroup (0, 0) also writes the route table and the permutation.
+//   gate/up : every workgroup redoes the routing of the T tokens it needs (no
+//             cross-workgroup state), picks its expert (the blockIdx.y-th active one),
+//             streams its rows and writes h in slot order; one extra workgroup, the last row
+//             of the grid, only routes and writes the route table and the permutation, so
+//             that this work is not added to any workgroup's weight stream.
 //   down    : one workgroup per tile of output rows loops over every active expert, keeps
 //             o for its rows in LDS and applies the combine (fixed order: routed j = 0..k-1,
 //             then shared, then residual) before writing y -- no o buffer, no combine launch.
@@ -181,7 +182,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
   // dispatched first); the routed experts take the rows from y0 on
   const int y0 = S > 0 ? nch : 0;
   const bool shared_wg = (int)blockIdx.y < y0;
-  const bool publisher = blockIdx.x == 0 && (int)blockIdx.y == y0;
+  const bool publisher = (int)blockIdx.y == (int)gridDim.y - 1;
+  if (publisher && blockIdx.x != 0) return;
   const bool fast1 = T == 1 && !publisher;
   if (shared_wg) {
     if (tid == 0) {
@@ -192,8 +194,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
     __syncthreads();
   } else if (fast1) {
     // one token: a routed workgroup needs only which expert is the target-th member of the
-    // top-k set in index order (its slot is that rank); order and weights are the
-    // publisher's business (it runs the full top-k below)
+    // top-k set in index order (its slot is that rank); order and weights are the route-table
+    // workgroup's business (it runs the full top-k)
     if (wave == 0) {
       const int target = (int)blockIdx.y - y0;
       const int e1 = wave_topk_member_any(logits, E, k, target);
@@ -241,6 +243,44 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
       }
     }
     __syncthreads();
+  }
+  if (publisher) {
+    // the route table and the permutation of the T tokens
+    int loc[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      run += b < NBIN ? s_cnt[b] : 0;
+      loc[i] = run;
+    }
+    int incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    lds_barrier();
+    int before = incl - run;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tid * 4 + i;
+      const int excl = before + (i ? loc[i - 1] : 0);
+      if (b < NBIN) { s_off[b] = excl; offsets_out[b] = excl; }
+      if (b == NBIN - 1) offsets_out[NBIN] = before + loc[i];
+    }
+    lds_barrier();
+    for (int p = tid; p < P; p += kDecThreads) {
+      const int id = s_ids[p];
+      int rank = 0;
+      for (int q = 0; q < p; ++q) rank += (s_ids[q] == id) ? 1 : 0;
+      const int slot = s_off[id] + rank;
+      sp_out[slot] = p;
+      ps_out[p] = slot;
+      ids_out[p] = id;
+      w_out[p] = s_w[p];
+    }
+    return;
   }
   const int e = s_e;
   if (e < 0) return;
@@ -294,44 +334,6 @@ __global__ void __launch_bounds__(kDecThreads) decode_gateup_kernel(
     for (int b = 0; b < BPL; ++b) {
       const int kb = lig + LPR * b;
       raw[p][b] = load_block(rowp, kb < NB ? kb : NB - 2 + (kb & 1));
-    }
-  }
-
-  // workgroup (0, y0), the first routed one, publishes the route table and the permutation
-  if (publisher) {
-    int loc[4], run = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tid * 4 + i;
-      run += b < NBIN ? s_cnt[b] : 0;
-      loc[i] = run;
-    }
-    int incl = run;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    lds_barrier();
-    int before = incl - run;
-    for (int w = 0; w < wave; ++w) before += s_wave[w];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tid * 4 + i;
-      const int excl = before + (i ? loc[i - 1] : 0);
-      if (b < NBIN) { s_off[b] = excl; offsets_out[b] = excl; }
-      if (b == NBIN - 1) offsets_out[NBIN] = before + loc[i];
-    }
-    lds_barrier();
-    for (int p = tid; p < P; p += kDecThreads) {
-      const int id = s_ids[p];
-      int rank = 0;
-      for (int q = 0; q < p; ++q) rank += (s_ids[q] == id) ? 1 : 0;
-      const int slot = s_off[id] + rank;
-      sp_out[slot] = p;
-      ps_out[p] = slot;
-      ids_out[p] = id;
-      w_out[p] = s_w[p];
     }
   }
 
@@ -720,7 +722,8 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   const int orows_wg = (kDecThreads / 64) * passes * (64 / gu.lpr) / 2;
   const int max_active = (int)std::min<int64_t>(sh.E, (int64_t)T * sh.k) + sh.S;
   const int tch = T;                               // every token of an expert in one workgroup
-  dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active * ((T + tch - 1) / tch));
+  // the last row of the grid is the route-table workgroup (only its column 0 stays)
+  dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active * ((T + tch - 1) / tch) + 1);
   const float* rs = use_norm ? sc.rscale : nullptr;
   bool ok;
   if (wide) {
