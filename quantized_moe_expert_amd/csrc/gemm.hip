@@ -60,7 +60,7 @@ constexpr int kBSlots = 4;               // weight-block register slots (filled 
 constexpr int kGemmThreads = 512;
 constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
 constexpr int kXcds = 8;                  // XCDs of an MI355X (each with its own L2)
-constexpr int kWin = 4;                   // A-fragment reads in flight, plus one
+constexpr int kWin = 6;                   // A-fragment reads in flight, plus one
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -238,46 +238,39 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = f32x16_t{};
 
-  // Issue order, pinned by scheduling barriers (the vmcnt count below depends on it): B(0) B(1)
-  // A(0), then B(j + 2) A(j + 1) in turn -- the prologue up to A(2), each step kt one pair
-  // B(kt + 4) A(kt + 3).
+  // Steps go in pairs (kt, kt + 1), kt even (K is a multiple of 128, so the step count is
+  // even): one wait and one barrier a pair, then the copies of the next pair's two stages,
+  // then the two steps; each step refills its weight slot.  Issue order, pinned by
+  // scheduling barriers (the vmcnt count depends on it): B(0) B(1) A(0) A(1) B(2) B(3), then a
+  // pair kt issues A(kt+2) A(kt+3) B(kt+4) B(kt+5).
   load_b(0, bq[0]);
   load_b(1, bq[1]);
   __builtin_amdgcn_sched_barrier(0);
   dma_a(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_b(2, bq[2]);
-  __builtin_amdgcn_sched_barrier(0);
   dma_a(1, 1);
   __builtin_amdgcn_sched_barrier(0);
+  load_b(2, bq[2]);
   load_b(3, bq[3]);
   __builtin_amdgcn_sched_barrier(0);
-  dma_a(2, 2);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // Step kt (U = kt % 4): wait until A(kt) has landed (issued after it: B(kt+2), A(kt+1),
-  // B(kt+3), A(kt+2) = 2 * 2 + 2 * NA instructions of this wave; B(kt) came before it), then
-  // a barrier: every wave's copies of A(kt) are in, and every wave has used its reads of
-  // stage (kt+3) % 4 from step kt - 1.  The barrier carries no memory fence: a workgroup
-  // release fence makes the compiler wait for every copy still in flight (vmcnt(0)), which
-  // would undo the prefetch; the explicit waits order the copies, the lgkmcnt(0) this wave's
-  // LDS reads, and the memory clobber keeps the compiler from moving LDS accesses across.
-  // The scheduling barrier after it keeps the first uses of B(kt) below the wait, where the
-  // compiler has nothing left to wait for.  Then take B(kt) out of slot U, refill slot U with
-  // B(kt+4) and stage (kt+3) % 4 with A(kt+3), multiply.  Every step issues the same
-  // instructions (step indices past the end are clamped), which the vmcnt count relies on.
-  constexpr int kOutstanding = 2 * 2 + 2 * NA;
-  auto body = [&](int kt, auto uc) __attribute__((always_inline)) {
+  // Pair kt (U = kt % 4, 0 or 2): wait until A(kt) and A(kt+1) have landed (issued after
+  // them: B(kt+2), B(kt+3) = 4 instructions of this wave; B(kt) and B(kt+1) came before),
+  // then a barrier: every wave's copies of both stages are in, and every wave has used its
+  // reads of stages (kt+2) % 4 and (kt+3) % 4 from the previous pair.  The barrier carries no
+  // memory fence: a workgroup release fence makes the compiler wait for every copy still in
+  // flight (vmcnt(0)), which would undo the prefetch; the explicit waits order the copies,
+  // the lgkmcnt(0) this wave's LDS reads, and the memory clobber keeps the compiler from
+  // moving LDS accesses across.  The scheduling barrier after it keeps the first uses of the
+  // weight slots below the wait, where the compiler has nothing left to wait for.  Every pair
+  // issues the same instructions (step indices past the end are clamped), which the vmcnt
+  // count relies on.
+  constexpr int kOutstanding = 2 * 2;
+  auto step = [&](int kt, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
-    wait_vm<kOutstanding>();
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
     const BlockTab tab = block_tab(bq[U], h != 0);
     uint32_t code[4];
     block_codes(bq[U], h != 0, code);
     load_b(kt + 4, bq[U]);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_a(kt + 3, (U + 3) % kStages);
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* stage = stage_of(U);
     // Matrix instruction j of the step (j < 4 RG): group I = j / RG (k 16 I .. 16 I + 15),
@@ -322,18 +315,25 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // whole groups of four steps in the loop, the remainder after it: no conditional step inside
-  // the loop, whose paths would again meet with different outstanding loads
+  auto pair = [&](int kt, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    wait_vm<kOutstanding>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(kt + 2, (U + 2) % kStages);
+    dma_a(kt + 3, (U + 3) % kStages);
+    __builtin_amdgcn_sched_barrier(0);
+    step(kt, std::integral_constant<int, U>{});
+    step(kt + 1, std::integral_constant<int, U + 1>{});
+  };
+  // whole groups of two pairs in the loop, the remainder (one pair) after it: no conditional
+  // step inside the loop, whose paths would meet with different outstanding loads
   int kt = 0;
   for (; kt + kStages <= NKT; kt += kStages) {
-    body(kt, std::integral_constant<int, 0>{});
-    body(kt + 1, std::integral_constant<int, 1>{});
-    body(kt + 2, std::integral_constant<int, 2>{});
-    body(kt + 3, std::integral_constant<int, 3>{});
+    pair(kt, std::integral_constant<int, 0>{});
+    pair(kt + 2, std::integral_constant<int, 2>{});
   }
-  if (kt < NKT) body(kt, std::integral_constant<int, 0>{});
-  if (kt + 1 < NKT) body(kt + 1, std::integral_constant<int, 1>{});
-  if (kt + 2 < NKT) body(kt + 2, std::integral_constant<int, 2>{});
+  if (kt < NKT) pair(kt, std::integral_constant<int, 0>{});
   wait_vm<0>();                           // no copy may land in LDS after the tile is done
 
   // epilogue: lane (c32, h) holds column c32 of each 32 x 32 tile; register e is row
