@@ -416,13 +416,15 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=8)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=128)
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the rocm-smi clock readings (for runs under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy 3 times (the reference kernel "
                          "of known traffic for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: bench.py measures one GPU "
               f"(the layer would shard by replicas or by experts across GPUs)", file=sys.stderr)
         sys.exit(2)
 
@@ -441,7 +443,7 @@ def main():
     M.lib()
     from synth.configs import XING4_DECODE, XING4_PREFILL, QWEN3NEXT_LIKE, DSV41_LIKE
 
-    clocks_before = gpu_clocks()
+    clocks_before = None if args.no_clocks else gpu_clocks()
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -499,7 +501,7 @@ def main():
         log(f"[bench] dsv41 prefill: GEMM {pd['gemm_tflops']:.1f} TFLOP/s")
         del stack, keep
         torch.cuda.empty_cache()
-    clocks_after = gpu_clocks()
+    clocks_after = None if args.no_clocks else gpu_clocks()
 
     gu_gbs = d["gate_up_gbs"]
     rec = {

@@ -63,7 +63,7 @@ typedef enum {
     MOE_ERR_NULL = 1,          /* a required pointer is NULL                              */
     MOE_ERR_SHAPE = 2,         /* a size is out of range or not a supported multiple      */
     MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() reported    */
-    MOE_ERR_UNSUPPORTED = 4,   /* an enum value or feature this build does not support    */
+    MOE_ERR_UNSUPPORTED = 4,   /* an enum value or feature the library does not support   */
     MOE_ERR_HIP = 5,           /* a HIP launch failed                                     */
     MOE_ERR_ALIGNMENT = 6,     /* a pointer or stride violates the alignment contract     */
     MOE_ERR_SCRATCH_LIMIT = 7  /* more scratch than moe_decode_layer_noalloc's array holds */

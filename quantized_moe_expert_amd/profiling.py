@@ -56,6 +56,7 @@ def stats_summary(stats_csv, command):
 
 def _per_kernel(path, counter):
     vals = defaultdict(list)
+    by_grid = defaultdict(list)
     calib = None
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
@@ -63,7 +64,8 @@ def _per_kernel(path, counter):
         if calib is None and "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 131072:
             calib = float(r["Counter_Value"])            # first dispatch: the 256 MiB copy
         vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
-    return vals, calib
+        by_grid[(_short(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return vals, calib, by_grid
 
 
 def _source_key(short):
@@ -74,8 +76,8 @@ def _source_key(short):
 
 
 def pmc_summary(fetch_csv, write_csv, commands):
-    fetch, cf = _per_kernel(fetch_csv, "FETCH_SIZE")
-    write, cw = _per_kernel(write_csv, "WRITE_SIZE")
+    fetch, cf, fetch_g = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write, cw, write_g = _per_kernel(write_csv, "WRITE_SIZE")
     if not cf or not cw:
         raise SystemExit("no calibration copy found (run bench.py with --copy-calibration)")
     sf = COPY_BYTES / (cf * 1024)
@@ -91,6 +93,13 @@ def pmc_summary(fetch_csv, write_csv, commands):
         if key:
             line += f" source_digest {source_digest(key)}"
         out.append(line)
+        grids = sorted(g for (kk, g) in fetch_g if kk == k and (kk, g) in write_g)
+        if len(grids) > 1:                 # one line a grid size: the launches of one shape
+            for g in grids:
+                fg, wg = fetch_g[(k, g)], write_g[(k, g)]
+                out.append(f"  grid {g}: dispatches {len(fg)}: fetch_bytes "
+                           f"{sum(fg) / len(fg) * 1024 * sf:.0f} write_bytes "
+                           f"{sum(wg) / len(wg) * 1024 * sw:.0f}")
     return "\n".join(out) + "\n"
 
 
@@ -111,18 +120,20 @@ def traffic(kernel, root):
 
 
 def counter_summary(csv_path, command, cu_count=256, xcds=8):
-    """Per kernel: the mean per dispatch of every counter in a rocprofv3 --pmc CSV, and the
+    """Per kernel and grid size: the mean per dispatch of every counter in a rocprofv3 --pmc CSV, and the
     ratios these counters define (LDS bank-conflict share of LDS cycles, MFMA busy share of
     SIMD cycles, LDS active share of CU cycles).  GRBM_GUI_ACTIVE reads as the sum over the
     XCDs (8 x the kernel's cycles), so the elapsed cycles are that value / xcds."""
     per = defaultdict(lambda: defaultdict(list))
     for r in csv.DictReader(open(csv_path)):
-        per[_short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    out = [f"command: {command}", ""]
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = [f"command: {command}", "",
+           "(one block a kernel and grid size: the launches of one workload shape)", ""]
     for k in sorted(per):
         c = {n: sum(v) / len(v) for n, v in per[k].items()}
         n = max(len(v) for v in per[k].values())
-        out.append(f"kernel {k}: dispatches {n}")
+        out.append(f"kernel {k[0]} grid {k[1]}: dispatches {n}")
         for name in sorted(c):
             out.append(f"  {name:28s} {c[name]:.4g}")
         if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"]:
