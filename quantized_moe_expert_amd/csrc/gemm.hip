@@ -13,10 +13,11 @@
 //
 //   activations  copied from HBM straight into LDS by the LDS-direct loads of gfx950
 //                (global_load_lds_dwordx4: no registers, no LDS write instructions), one
-//                instruction per 8 whole rows (coalesced), into a ring of 4 stages filled 3
-//                steps ahead, the copies of a step spread evenly over the eight waves; the
-//                16-byte chunks of a row are XOR-swizzled so that every fragment read is a
-//                conflict-free ds_read_b128, and the reads run three matrix instructions
+//                instruction per 8 whole rows (coalesced), into a ring of 4 stages filled
+//                two and three steps ahead (K steps go in pairs, one wait and one barrier a
+//                pair), the copies of a step spread evenly over the eight waves; the 16-byte
+//                chunks of a row are XOR-swizzled so that every fragment read is a
+//                conflict-free ds_read_b128, and the reads run five matrix instructions
 //                ahead of their use;
 //   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, 4 steps
 //                ahead (a ring of 4 register slots), and dequantises them there; each weight
@@ -55,7 +56,7 @@ namespace moe {
 constexpr int kBM = 256;                 // slot rows per tile
 constexpr int kBN = 256;                 // weight rows per tile
 constexpr int kKS = 64;                  // k per step (2 IQ4_NL blocks)
-constexpr int kStages = 4;               // activation stages in LDS (filled 3 steps ahead)
+constexpr int kStages = 4;               // activation stages in LDS (filled 2-3 steps ahead)
 constexpr int kBSlots = 4;               // weight-block register slots (filled 4 steps ahead)
 constexpr int kGemmThreads = 512;
 constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
@@ -123,8 +124,8 @@ __device__ __forceinline__ bf16x8_t b_frag(const uint32_t (&c)[4], const BlockTa
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// s_waitcnt vmcnt(N): every vector-memory instruction of this wave but the last N issued has
-// completed (they complete in issue order)
+// s_waitcnt vmcnt(N): at most N vector-memory instructions of this wave are outstanding.
+// Loads into registers complete in issue order; LDS-direct copies are waited for with N = 0.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -253,10 +254,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
   load_b(3, bq[3]);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Pair kt (U = kt % 4, 0 or 2): wait until A(kt) and A(kt+1) have landed (issued after
-  // them: B(kt+2), B(kt+3) = 4 instructions of this wave; B(kt) and B(kt+1) came before),
-  // then a barrier: every wave's copies of both stages are in, and every wave has used its
-  // reads of stages (kt+2) % 4 and (kt+3) % 4 from the previous pair.  The barrier carries no
+  // Pair kt (U = kt % 4, 0 or 2): wait until every load of this wave has completed (A(kt)
+  // and A(kt+1) among them), then a barrier: every wave's copies of both stages are in, and
+  // every wave has used its reads of stages (kt+2) % 4 and (kt+3) % 4 from the previous pair.
+  // The wait is a full one (vmcnt(0)): the LDS-direct copies need not complete in issue
+  // order, and a wait for all but the last N loads did not order them -- a producer/consumer
+  // version whose waits let later copies stay in flight read stale activations.  Here the
+  // loads still in flight at a pair's wait are the previous pair's last weight blocks, so the
+  // full wait costs about 4%.  The barrier carries no
   // memory fence: a workgroup release fence makes the compiler wait for every copy still in
   // flight (vmcnt(0)), which would undo the prefetch; the explicit waits order the copies,
   // the lgkmcnt(0) this wave's LDS reads, and the memory clobber keeps the compiler from
@@ -264,7 +269,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
   // weight slots below the wait, where the compiler has nothing left to wait for.  Every pair
   // issues the same instructions (step indices past the end are clamped), which the vmcnt
   // count relies on.
-  constexpr int kOutstanding = 2 * 2;
+  constexpr int kOutstanding = 0;
   auto step = [&](int kt, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
     const BlockTab tab = block_tab(bq[U], h != 0);
