@@ -46,9 +46,45 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic(kernel):
+def traffic(kernel, grid=None):
     from quantized_moe_expert_amd import profiling
-    return profiling.traffic(kernel, ROOT)
+    return profiling.traffic(kernel, ROOT, grid)
+
+
+def _lanes_blocks(nb):
+    """Lanes a weight row and blocks a lane the decode kernels pick for rows of nb blocks
+    (least idle lanes, at most 4 blocks a lane): the template arguments of the kernel."""
+    best, waste = None, 1 << 30
+    for lpr in (64, 32, 16, 8, 4):
+        bpl = -(-nb // lpr)
+        if bpl <= 4 and lpr * bpl - nb < waste:
+            best, waste = (lpr, bpl), lpr * bpl - nb
+    return best
+
+
+def add_gemm_traffic(record, wl):
+    """The grouped GEMMs' HBM bytes a launch (copy-calibrated counters of the profiles/
+    summary, for this workload's grid) next to their algorithmic bytes."""
+    T = wl.prefill_tokens[0]
+    s = wl.shape
+    rows = T * (s.top_k + s.n_shared)
+    experts = min(s.n_experts, T * s.top_k) + s.n_shared          # upper bound on active
+    for stage, key, w_bytes, io in ((0, "gate_up", 2 * s.gate_bytes,
+                                     rows * s.hidden * 2 + rows * s.ffn * 2),
+                                    (1, "down", s.down_bytes,
+                                     rows * s.ffn * 2 + rows * s.hidden * 4)):
+        t = traffic("gemm_kernel<%s>" % ("true" if stage == 0 else "false"),
+                    gemm_grid(s, T, stage))
+        record[f"{key}_traffic_bytes"] = t
+        record[f"{key}_algorithmic_bytes_max"] = experts * w_bytes + io
+
+
+def gemm_grid(shape, tokens, stage):
+    """Threads of a grouped-GEMM launch (the tile bound the library launches)."""
+    rows = tokens * (shape.top_k + shape.n_shared)
+    mtiles = -(-rows // 256) + min(shape.n_experts + shape.n_shared, rows)
+    nt = shape.ffn // 128 if stage == 0 else -(-shape.hidden // 256)
+    return -(-mtiles * nt // 8) * 8 * 512
 
 
 # ---- CPU baseline (the oracle), run before the GPU is touched ----------------------------
@@ -485,6 +521,7 @@ def main():
             log(f"[bench] qwen3next decode T={T}: {dq['tok_s']:.1f} tok/s")
         pq = prefill_bench(QWEN3NEXT_LIKE, stack[0], args.prefill_reps)
         configs.append(prefill_record("qwen3next_like", QWEN3NEXT_LIKE, pq))
+        add_gemm_traffic(configs[-1], QWEN3NEXT_LIKE)
         log(f"[bench] qwen3next prefill: GEMM {pq['gemm_tflops']:.1f} TFLOP/s, "
             f"{pq['gemm_gbs']:.0f} GB/s")
         del stack, keep
@@ -498,6 +535,7 @@ def main():
         log(f"[bench] dsv41 decode T=16: {dd['tok_s']:.1f} tok/s")
         pd = prefill_bench(DSV41_LIKE, stack[0], max(2, args.prefill_reps // 2))
         configs.append(prefill_record("dsv41_like", DSV41_LIKE, pd))
+        add_gemm_traffic(configs[-1], DSV41_LIKE)
         log(f"[bench] dsv41 prefill: GEMM {pd['gemm_tflops']:.1f} TFLOP/s")
         del stack, keep
         torch.cuda.empty_cache()
@@ -530,7 +568,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-            "traffic": (traffic("decode_gateup_kernel")
+            "traffic": (traffic("decode_gateup_kernel<%d, %d, 1, 4>"
+                                % _lanes_blocks(XING4_DECODE.shape.hidden // 32))
                         if d["T"] == 1 else None),
             "bytes_per_launch": round(d["gate_up_bytes"]),
             "avg_launch_us": round(d["stage_us"]["gate_up"], 3),
@@ -541,8 +580,7 @@ def main():
     }
     if prefill_main:
         rec["prefill"] = prefill_record("xing4_prefill", XING4_PREFILL, prefill_main)
-        rec["prefill"]["gate_up_traffic_bytes"] = traffic("gemm_kernel<true>")
-        rec["prefill"]["down_traffic_bytes"] = traffic("gemm_kernel<false>")
+        add_gemm_traffic(rec["prefill"], XING4_PREFILL)
     if configs:
         rec["configs"] = configs
     if cpu:

@@ -27,7 +27,7 @@ KERNEL_SOURCES = {
     "gemm_kernel<true>": ("gemm.hip", "common.h", "kernels.h"),
     "gemm_kernel<false>": ("gemm.hip", "common.h", "kernels.h"),
 }
-PMC_FILE = "pmc_traffic_xing4.txt"
+PMC_FILE = "pmc_traffic_decode_and_prefill_all_workloads.txt"
 
 
 def source_digest(kernel):
@@ -103,20 +103,34 @@ def pmc_summary(fetch_csv, write_csv, commands):
     return "\n".join(out) + "\n"
 
 
-def traffic(kernel, root):
-    """HBM bytes a dispatch (fetch + write) recorded for `kernel`, or None if missing/stale."""
+def traffic(kernel, root, grid=None):
+    """HBM bytes a dispatch (fetch + write) recorded for `kernel` -- a short kernel name with
+    its template arguments as the summary prints it, e.g. ``decode_gateup_kernel<64, 2, 1, 4>``
+    -- at grid size `grid` (threads; None: the kernel's mean over all its dispatches), or None
+    if missing or recorded from other sources."""
     path = os.path.join(root, "profiles", PMC_FILE)
     if not os.path.exists(path):
         return None
-    pat = re.compile(r"^kernel (.+): dispatches \d+: fetch_bytes (\d+) write_bytes (\d+)"
-                     r" source_digest (\w+)")
+    head = re.compile(r"^kernel (.+): dispatches \d+: fetch_bytes (\d+) write_bytes (\d+)"
+                      r" source_digest (\w+)")
+    sub = re.compile(r"^\s+grid (\d+): dispatches \d+: fetch_bytes (\d+) write_bytes (\d+)")
+    cur = None
     for line in open(path):
-        m = pat.match(line.strip())
-        if m and _source_key(m.group(1)) == kernel:
-            if m.group(4) != source_digest(kernel):
-                return None
+        m = head.match(line)
+        if m:
+            cur = None
+            if m.group(1) == kernel:
+                key = _source_key(kernel)
+                if key is None or m.group(4) != source_digest(key):
+                    return None
+                cur = int(m.group(2)) + int(m.group(3))
+                if grid is None:
+                    return cur
+            continue
+        m = sub.match(line)
+        if m and cur is not None and int(m.group(1)) == grid:
             return int(m.group(2)) + int(m.group(3))
-    return None
+    return cur if grid is None else None
 
 
 def counter_summary(csv_path, command, cu_count=256, xcds=8):
