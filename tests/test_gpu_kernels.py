@@ -397,6 +397,38 @@ def test_grouped_gemm_against_oracle(name, T, stage):
             assert_close(got[a:b][:, sample], ref, REL_L2_MFMA, f"{name} e={e} {stage}")
 
 
+@pytest.mark.parametrize("stage", ["gate_up", "down"])
+def test_grouped_gemm_reruns_bit_identical(stage):
+    """The grouped GEMM is deterministic: eight launches on the same 2,048-token chunk of the
+    3584/64 shape (every expert routed; partial and full tiles) give the same bits.  A copy into LDS read before it has landed, or a stage overwritten while still
+    read, shows up here as a run that differs."""
+    wl = WORKLOADS["xing4_prefill"]
+    s = wl.shape
+    T = 2048
+    rng = np.random.default_rng(zlib.crc32(f"gemm-reruns/{stage}".encode()))
+    x, ids, w, off, sp, ps = _route_table(wl, T, rng)
+    rows = T * s.top_k + T
+    used = sorted(set(ids.reshape(-1).tolist()) | {s.n_experts})
+    bank_t, bank = L.make_bank(wl, 0, experts=used)
+    desc = L.desc_of(s, T)
+    K, nout = (s.hidden, s.ffn) if stage == "gate_up" else (s.ffn, s.hidden)
+    xin = _bf16_tensor((rng.standard_normal((rows, K)) * 0.7).astype(np.float32))
+    dt = torch.bfloat16 if stage == "gate_up" else torch.float32
+    st = M.MOE_STAGE_GATE_UP if stage == "gate_up" else M.MOE_STAGE_DOWN
+    offd = _to_dev(off)
+    outs = []
+    for _ in range(8):
+        out = torch.full((rows, nout), np.nan, dtype=dt, device=DEV)
+        M.moe_grouped_gemm_iq4nl(desc, st, bank, offd, xin, out, T)
+        outs.append(out)
+    torch.cuda.synchronize()
+    ref = outs[0].view(torch.int16 if stage == "gate_up" else torch.int32)
+    assert torch.isfinite(outs[0].float()).all()
+    for i, o in enumerate(outs[1:], 1):
+        same = torch.equal(o.view(ref.dtype), ref)
+        assert same, f"run {i} differs from run 0 ({stage})"
+
+
 def _bf16_cpu(a):
     """fp32 [rows, K] -> bf16 tensor on the device, rounded on the host by torch (RNE)."""
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(DEV)
