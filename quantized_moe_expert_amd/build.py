@@ -17,12 +17,15 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result"]
+# per-source additions: the batched decode kernels keep their small matrix results in VGPRs
+# (read by VALU right after each instruction) instead of AGPRs that need a copy each
+EXTRA_FLAGS = {"bdecode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 LIBS = {
     os.path.join(PKG, "libmoe_iq4nl.so"): [
         os.path.join(PKG, "csrc", f) for f in
         ("api.hip", "quant.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip",
-         "combine.hip", "decode.hip")],
+         "combine.hip", "decode.hip", "bdecode.hip")],
     os.path.join(ROOT, "synth", "libmoe_synth.so"): [
         os.path.join(ROOT, "synth", "csrc", "synth.hip")],
 }
@@ -43,7 +46,7 @@ def source_digest(lib):
 
 
 def _compile(src, obj, verbose):
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -100,9 +100,11 @@ Shape shape_of(const moe_desc* d) {
 size_t logits_bytes(const moe_desc* d, int32_t T) { return align256((size_t)T * d->n_experts * 4); }
 
 // Fused decode layer: header | logits | rscale | ids | w | offsets | sorted_pairs | pair_slot |
-// h | o (o only when down + combine cannot be fused).
+// h | xn.  For the batched kernels (above kDecodeFusedMaxT tokens, or when the down stage's
+// LDS cannot hold every slot's h) xn and h hold bf16 (hi, lo) pair rows: the same bytes as
+// fp32 rows.
 struct DecodeLayout {
-  size_t logits, rscale, ids, w, offsets, sp, ps, h, xn, o, total;
+  size_t logits, rscale, ids, w, offsets, sp, ps, h, xn, total;
 };
 
 DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
@@ -119,11 +121,6 @@ DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
   L.ps = off; off += align256(P * 4);
   L.h = off; off += align256(rows * d->ffn * 4);
   L.xn = off; off += align256((size_t)T * d->hidden * 4);
-  L.o = off;
-  if (T > moe::kDecodeFusedMaxT ||
-      !moe::decode_down_fused_fits(Shape{d->hidden, d->ffn, d->n_experts, d->top_k,
-                                         d->n_shared, d->gating, d->renormalize}, T))
-    off += align256(rows * d->hidden * 4);
   L.total = off;
   return L;
 }
@@ -340,7 +337,6 @@ moe_status run_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   sc.sorted_pairs = reinterpret_cast<int32_t*>(b + L.sp);
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
-  sc.o = reinterpret_cast<float*>(b + L.o);
   sc.xn = reinterpret_cast<float*>(b + L.xn);
   sc.count = reinterpret_cast<int32_t*>(b);
   return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
@@ -414,7 +410,6 @@ moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32
   sc.sorted_pairs = reinterpret_cast<int32_t*>(b + L.sp);
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
-  sc.o = reinterpret_cast<float*>(b + L.o);
   sc.xn = reinterpret_cast<float*>(b + L.xn);
   sc.count = reinterpret_cast<int32_t*>(b);
   for (int32_t l = 0; l < n_layers; ++l) {

@@ -1,0 +1,708 @@
+// Batched decode layer (5 to 16 tokens) in three launches, the expert products on the bf16
+// matrix cores (v_mfma_f32_16x16x32_bf16) with exact codebook values.
+//
+// PocketLLM "Xing4.0-29B-A4B", section "Known limitations": a decode step is bound by its launch
+// count, so a layer should be a few large kernels; Red Lite "What we learned", section "1. The
+// idea": the whole token is routed on the GPU, with no host round trip; section "4. Speculative
+// decoding": a weight block is decoded once for all the token rows that use it.
+//
+//   router  (decode_router_kernel, decode.hip): the logits of the T tokens, and each token's row
+//           scaled by its RMSNorm factor and split into bf16 (hi, lo) pairs in code-byte order.
+//   gate/up (bdec_gateup_kernel): one workgroup per (expert, 64 or 128 FFN rows).  It finds the
+//           tokens that picked its expert by counting, for each token, the experts ranked above
+//           the expert (fewer than k: picked, and that count is its place j in the token's
+//           list), so no workgroup waits for another.  h leaves as bf16 (hi, lo) pairs in pair
+//           order (row t * k + j; the shared expert's rows after the P routed ones).  The grid's
+//           last row holds one workgroup that runs the full top-k, the gating weights, the
+//           route table and the permutation.
+//   down    (bdec_down_kernel): one workgroup per 16 output rows over every active expert; o
+//           of every slot for those rows stays in LDS and the combine (fixed order: routed
+//           j = 0..k-1, the shared expert, the residual) writes y.
+//
+// Matrix products.  An expert's tokens (at most 16: a token picks an expert once) are the 16
+// rows of the A operand and 16 weight rows the columns of B.  One instruction covers one IQ4_NL
+// block (K = 32) of those rows, so its fp32 result is scaled by the block's d before it is
+// added up: the arithmetic of the dequant-GEMV (exact codebook values times the bf16 hi and lo
+// parts of the activations, fp32 sums a block, scaled by d in fp32).  Inside a block the K
+// order is the code-byte order: lane quarter g holds code bytes 4g..4g+3 of its row's block,
+// each byte standing for the pair (element j, element j + 16).  B is then one lookup of a
+// 256-entry table of bf16 pairs a byte, and A one 16-byte load of the pre-split pairs.
+//
+// Weights are read a block pair (36 bytes, dword aligned) at a time: lane quarter g loads dwords
+// g, g + 1 (the even block's code bytes 4g..4g+3 straddle them) and 4 + g, 5 + g (the odd
+// block's, dword 5 + g); the first quarter also holds both scales (dwords 0 and 4), which one
+// lane permute hands to the other three quarters.
+#include "common.h"
+#include "kernels.h"
+#include "route_core.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBdThreads = 256;        // gate/up workgroup
+constexpr int kBdDownWaves = 8;        // down workgroup: 8 waves share the experts
+constexpr int kBdMaxK = 32;
+constexpr uint32_t kOob = 0x80000000u; // buffer offset past every range: the load returns 0
+constexpr int kNt = 0;                  // cache policy of the weight loads: default (a 128-byte
+                                        // line is read by several instructions: it must stay)
+
+// Buffer resource over `bytes` bytes from `base`; loads past the end return zeros and touch no
+// memory (the rows of A past an expert's tokens).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Four dwords of one weight row's block pair for lane quarter q: dwords q, q + 1, 4 + q, 5 + q
+// of the pair; `off` is the byte offset of dword q (buffer loads).
+__device__ __forceinline__ void load_bpair(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                           uint32_t (&w)[4]) {
+  const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, kNt);
+  const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(off + 16u), 0, kNt);
+  w[0] = a[0];
+  w[1] = a[1];
+  w[2] = b[0];
+  w[3] = b[1];
+}
+
+// B operand of four code bytes: the bf16 pairs of their codebook values.
+__device__ __forceinline__ bf16x8_t b_pairs(uint32_t cw, const uint32_t* s_tab) {
+  u32x4_t v;
+  v[0] = s_tab[cw & 0xFFu];
+  v[1] = s_tab[(cw >> 8) & 0xFFu];
+  v[2] = s_tab[(cw >> 16) & 0xFFu];
+  v[3] = s_tab[cw >> 24];
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// acc += d_even * (A_even . B_even) + d_odd * (A_odd . B_odd) for one block pair of one tile of
+// 16 weight rows; ah / al: the hi and lo activation fragments of the two blocks.  keep = false
+// (a block pair past the end, loaded again so that no branch surrounds the loads) zeroes both
+// scales: the pair then adds exactly zero.
+__device__ __forceinline__ void tile_pair(const uint32_t (&w)[4], const bf16x8_t (&ah)[2],
+                                          const bf16x8_t (&al)[2], const uint32_t* s_tab,
+                                          int c16, bool keep, f32x4_t& acc) {
+  // scales: dword 0 low half (even block) and dword 4 high half (odd block) of quarter 0
+  uint32_t dd = __shfl(__builtin_amdgcn_perm(w[2], w[0], 0x07060100u), c16, 64);
+  dd = keep ? dd : 0u;
+  const float d0 = __half2float(__ushort_as_half((unsigned short)(dd & 0xFFFFu)));
+  const float d1 = __half2float(__ushort_as_half((unsigned short)(dd >> 16)));
+  const bf16x8_t b0 = b_pairs(__builtin_amdgcn_alignbit(w[1], w[0], 16), s_tab);
+  const bf16x8_t b1 = b_pairs(w[3], s_tab);
+  const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[0], b0, z, 0, 0, 0);
+  p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[0], b0, p0, 0, 0, 0);
+  f32x4_t p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[1], b1, z, 0, 0, 0);
+  p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[1], b1, p1, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(d1, p1[r], fmaf(d0, p0[r], acc[r]));
+}
+
+// tile_pair with the block pair's 9 dwords in LDS at rw (the weights staged by the
+// workgroup): dwords q, q + 1 (the even block's code bytes 4q..4q+3 straddle them), 5 + q
+// (the odd block's), and the scales in dwords 0 (low half) and 4 (high half).
+__device__ __forceinline__ void tile_pair_lds(const uint32_t* rw, int q, const bf16x8_t (&ah)[2],
+                                              const bf16x8_t (&al)[2], const uint32_t* s_tab,
+                                              f32x4_t& acc) {
+  const uint32_t w0 = rw[q], w1 = rw[q + 1], w3 = rw[5 + q];
+  const uint32_t dd = __builtin_amdgcn_perm(rw[4], rw[0], 0x07060100u);
+  const float d0 = __half2float(__ushort_as_half((unsigned short)(dd & 0xFFFFu)));
+  const float d1 = __half2float(__ushort_as_half((unsigned short)(dd >> 16)));
+  const bf16x8_t b0 = b_pairs(__builtin_amdgcn_alignbit(w1, w0, 16), s_tab);
+  const bf16x8_t b1 = b_pairs(w3, s_tab);
+  const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[0], b0, z, 0, 0, 0);
+  p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[0], b0, p0, 0, 0, 0);
+  f32x4_t p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[1], b1, z, 0, 0, 0);
+  p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[1], b1, p1, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(d1, p1[r], fmaf(d0, p0[r], acc[r]));
+}
+
+// Activation fragments of block pair bp: row offset `aoff` (bytes, or kOob: zeros), 128 bytes a
+// block (16 hi pair dwords, then 16 lo).  The loads are buffer loads as well, so that the
+// compiler keeps them where they are issued.
+__device__ __forceinline__ void load_apair(__amdgpu_buffer_rsrc_t rs, uint32_t aoff, int bp,
+                                           u32x4_t (&a)[4]) {
+  const uint32_t o = aoff + (uint32_t)bp * 256u;      // kOob + 511 is still past every range
+  a[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
+  a[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 64u), 0, 0);
+  a[2] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 128u), 0, 0);
+  a[3] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 192u), 0, 0);
+}
+
+// The route table of T tokens by one workgroup of 256 threads: top-k and gating weights of
+// every token (route_core.h), the slot counts, offsets, and the permutation (slots of an expert
+// in ascending pair order; the shared expert's slots P + t).
+__device__ void publish_routes(const float* __restrict__ logits, int T, int E, int S, int k,
+                               int gating, int renorm, int32_t* __restrict__ ids_out,
+                               float* __restrict__ w_out, int32_t* __restrict__ offsets_out,
+                               int32_t* __restrict__ sp_out, int32_t* __restrict__ ps_out,
+                               int* s_ids, float* s_w, int* s_cnt, int* s_off, int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int P = T * k, NBIN = E + S;
+  for (int i = tid; i < NBIN; i += kBdThreads) s_cnt[i] = 0;
+  for (int t = wave; t < T; t += kBdThreads / 64)
+    wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
+  __syncthreads();
+  for (int p = tid; p < P; p += kBdThreads) atomicAdd(&s_cnt[s_ids[p]], 1);
+  if (tid < S) s_cnt[E + tid] = T;
+  __syncthreads();
+  // exclusive scan of the NBIN <= 1024 counts, four bins a thread
+  int loc[4], run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = tid * 4 + i;
+    run += b < NBIN ? s_cnt[b] : 0;
+    loc[i] = run;
+  }
+  int incl = run;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int before = incl - run;
+  for (int w = 0; w < wave; ++w) before += s_wave[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = tid * 4 + i;
+    const int excl = before + (i ? loc[i - 1] : 0);
+    if (b < NBIN) {
+      s_off[b] = excl;
+      offsets_out[b] = excl;
+    }
+    if (b == NBIN - 1) offsets_out[NBIN] = before + loc[i];
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += kBdThreads) {
+    const int id = s_ids[p];
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += (s_ids[q] == id) ? 1 : 0;
+    const int slot = s_off[id] + rank;
+    sp_out[slot] = p;
+    ps_out[p] = slot;
+    ids_out[p] = id;
+    w_out[p] = s_w[p];
+  }
+}
+
+// ---- gate/up ---------------------------------------------------------------------------
+
+// The tokens of gate/up workgroup row y (expert y < E, or the shared expert for y >= E) into
+// s_tok (ascending token order) and their h rows into s_prow (pair t * k + j, or P + t), the
+// count into *s_m; 256 threads.  A routed expert's rank in token t's order (the keys of
+// route_core.h, ties to the lower index) is counted by 16 threads a token, each over the
+// experts e2 = sub, sub + 16, ...: below k it is picked, at place j = rank.
+__device__ __forceinline__ void route_expert(const float* __restrict__ logits, int T, int E,
+                                             int k, int y, int* s_rank, int* s_tok, int* s_prow,
+                                             int* s_m) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = T * k;
+  int& s_m_ref = *s_m;
+  if (y < E) {
+    // rank of expert y in each token's order (keys of route_core.h, ties to the lower index):
+    // 16 threads a token, each counting the experts e2 = sub, sub + 16, ... ranked above y
+    const int t = tid >> 4, sub = tid & 15;
+    int cnt = 0;
+    if (t < T) {
+      const float* lrow = logits + (size_t)t * E;
+      const uint32_t ky = order_bits(lrow[y]);
+      for (int e2 = sub; e2 < E; e2 += 16) {
+        const uint32_t kk = order_bits(lrow[e2]);
+        cnt += (kk > ky || (kk == ky && e2 < y)) ? 1 : 0;
+      }
+    }
+    cnt = (int)group_sum_dpp<16>((float)cnt);     // small integers: exact
+    if (sub == 0) s_rank[t] = (t < T && cnt < k) ? cnt : -1;
+    __syncthreads();
+    if (wave == 0) {
+      const int rk = lane < kDecodeMaxTokens ? s_rank[lane] : -1;
+      const uint64_t mask = __ballot(rk >= 0);
+      if (rk >= 0) {
+        const int i = __popcll(mask & ((1ull << lane) - 1));
+        s_tok[i] = lane;
+        s_prow[i] = lane * k + rk;
+      }
+      if (lane == 0) s_m_ref = __popcll(mask);
+    }
+  } else {                                 // the shared expert: every token, rows P + t
+    if (tid < T) {
+      s_tok[tid] = tid;
+      s_prow[tid] = P + tid;
+    }
+    if (tid == 0) s_m_ref = T;
+  }
+  __syncthreads();
+}
+
+
+// TP: tiles of 16 FFN rows a wave (each a gate and an up tile); D: block pairs in flight.
+template <int TP, int D>
+__global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ xhl,
+    const float* __restrict__ logits, int T, int H, int F, int E, int S, int k, int gating,
+    int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
+    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl) {
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_rank[kDecodeMaxTokens];
+  __shared__ int s_tok[kDecodeMaxTokens];
+  __shared__ int s_prow[kDecodeMaxTokens];
+  __shared__ int s_m;
+  __shared__ int s_ids[kDecodeMaxTokens * kBdMaxK];
+  __shared__ float s_w[kDecodeMaxTokens * kBdMaxK];
+  __shared__ int s_cnt[kMaxE + 1];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_wave[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int P = T * k;
+  const int y = blockIdx.y;
+  if (y == E + S) {                       // the route-table workgroup (grid column 0 only)
+    if (blockIdx.x == 0)
+      publish_routes(logits, T, E, S, k, gating, renorm, ids_out, w_out, offsets_out, sp_out,
+                     ps_out, s_ids, s_w, s_cnt, s_off, s_wave);
+    return;
+  }
+  s_tab[tid] = pair_table_entry(tid);
+  route_expert(logits, T, E, k, y, s_rank, s_tok, s_prow, &s_m);
+  const int m = s_m;
+  if (m == 0) return;
+  const int ex = y < E ? y : E;
+
+  const int NBH = H >> 5, NBF = F >> 5;
+  const int ti0 = ((int)blockIdx.x * (kBdThreads / 64) + wave) * TP;   // first tile of the wave
+  if ((ti0 >> 1) >= NBF) return;
+  const int c16 = lane & 15, q = lane >> 4;
+  const uint32_t rowb = (uint32_t)NBH * kBlockBytes;
+  // the expert's gate and up matrices (2 F rows) as one buffer
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(bank + (int64_t)ex * stride, 2u * F * rowb);
+  // tile ti: FFN block ti / 2, half ti % 2; column c16 is FFN row 32 (ti / 2) + 8 (ti % 2) +
+  // (c16 % 8) + 16 (c16 / 8), so that a row and the row 16 above it (one code-byte pair of h)
+  // sit in lanes c16 and c16 + 8
+  uint32_t rows[2 * TP];                    // byte offsets of dword q of the rows' first pair
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) {
+    const int ti = ti0 + tp;
+    const uint32_t f = 32 * (ti >> 1) + 8 * (ti & 1) + (c16 & 7) + 16 * (c16 >> 3);
+    rows[tp] = f * rowb + 4u * q;
+    rows[TP + tp] = (F + f) * rowb + 4u * q;
+  }
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xhl, (uint32_t)T * (uint32_t)H * 4u);
+  const uint32_t aoff = c16 < m ? (uint32_t)s_tok[c16] * (uint32_t)NBH * 128u + 16u * q : kOob;
+
+  const int NP = NBH >> 1;                  // block pairs a row
+  f32x4_t acc[2 * TP];
+#pragma unroll
+  for (int i = 0; i < 2 * TP; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t wr[D][2 * TP][4];
+  u32x4_t ar[D][4];
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int bp = u < NP ? u : NP - 1;
+#pragma unroll
+    for (int i = 0; i < 2 * TP; ++i) load_bpair(wrs, rows[i] + 36u * bp, wr[u][i]);
+    load_apair(xrs, aoff, bp, ar[u]);
+    __builtin_amdgcn_sched_barrier(0);      // the slots are issued in order
+  }
+  for (int b0 = 0; b0 < NP; b0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int bp = b0 + u;
+      {
+        const bf16x8_t ah[2] = {__builtin_bit_cast(bf16x8_t, ar[u][0]),
+                                __builtin_bit_cast(bf16x8_t, ar[u][2])};
+        const bf16x8_t al[2] = {__builtin_bit_cast(bf16x8_t, ar[u][1]),
+                                __builtin_bit_cast(bf16x8_t, ar[u][3])};
+#pragma unroll
+        for (int i = 0; i < 2 * TP; ++i)
+          tile_pair(wr[u][i], ah, al, s_tab, c16, bp < NP, acc[i]);
+      }
+      const int nb = bp + D < NP ? bp + D : NP - 1;
+#pragma unroll
+      for (int i = 0; i < 2 * TP; ++i) load_bpair(wrs, rows[i] + 36u * nb, wr[u][i]);
+      load_apair(xrs, aoff, nb, ar[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // h = silu(g) * u; lane c16 < 8 takes the row 16 above from lane c16 + 8 and writes the
+  // (hi, lo) pair dwords of both rows
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) {
+    const int ti = ti0 + tp;
+    const int j = 8 * (ti & 1) + c16;              // pair index inside the FFN block (c16 < 8)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float hv = silu(acc[tp][r]) * acc[TP + tp][r];
+      const float hu = dpp_f<0x128>(hv);           // row_ror:8: the value of lane c16 ^ 8
+      const int i = 4 * q + r;
+      if (c16 < 8 && i < m) {
+        uint32_t hi, lo;
+        split_pair(hv, hu, hi, lo);
+        uint32_t* dst = hhl + ((size_t)s_prow[i] * NBF + (ti >> 1)) * 32 + j;
+        dst[0] = hi;
+        dst[16] = lo;
+      }
+    }
+  }
+}
+
+
+// Workgroup-cooperative variant: the 4 waves take 64 FFN rows (a gate and an up tile each) and
+// walk K in steps of S block pairs together.  Each step's weights (128 rows x 36 S bytes) and
+// activations (up to 16 token rows x 2 S blocks x 128 bytes) are fetched as whole 16-byte
+// pieces of contiguous memory by all 256 threads, two steps ahead into registers, then written
+// to one of two LDS stages; one barrier a step; the waves read their operands from LDS.  Every
+// cache line of the weights is then read by one instruction, where the direct variant above
+// reads 20 bytes of each of 16 rows an instruction.  Needs rows of a multiple of 16 bytes and
+// whole steps (H / 64 a multiple of S, S a multiple of 4).
+template <int S>
+__global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ xhl,
+    const float* __restrict__ logits, int T, int H, int F, int E, int NS, int k, int gating,
+    int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
+    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl) {
+  static_assert(S % 4 == 0, "16-byte pieces of a step need S a multiple of 4");
+  constexpr int PPR = 9 * S / 4;                   // 16-byte pieces of a weight row a step
+  constexpr int NPB = 128 * PPR;                   // weight pieces a step
+  constexpr int NIB = (NPB + kBdThreads - 1) / kBdThreads;
+  constexpr int PPA = 16 * S;                      // 16-byte pieces of a token row a step
+  constexpr int NIA = kDecodeMaxTokens * PPA / kBdThreads;
+  constexpr int SB = 128 * 36 * S;                 // weight stage bytes
+  constexpr int AROW = 256 * S + 16;               // token row of an activation stage (padded:
+                                                   // the 16 rows of a fragment read hit
+                                                   // distinct banks)
+  constexpr int STG = SB + kDecodeMaxTokens * AROW;
+  static_assert(2 * STG >= (int)(2 * kDecodeMaxTokens * kBdMaxK * 4 + 2 * (kMaxE + 1) * 4 + 16),
+                "the route-table workgroup's arrays share the stage memory");
+  __shared__ __align__(16) uint8_t s_mem[2 * STG];
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_rank[kDecodeMaxTokens];
+  __shared__ int s_tok[kDecodeMaxTokens];
+  __shared__ int s_prow[kDecodeMaxTokens];
+  __shared__ int s_m;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int y = blockIdx.y;
+  if (y == E + NS) {                      // the route-table workgroup (grid column 0 only)
+    if (blockIdx.x == 0) {
+      int* s_ids = reinterpret_cast<int*>(s_mem);
+      float* s_w = reinterpret_cast<float*>(s_ids + kDecodeMaxTokens * kBdMaxK);
+      int* s_cnt = reinterpret_cast<int*>(s_w + kDecodeMaxTokens * kBdMaxK);
+      int* s_off = s_cnt + kMaxE + 1;
+      int* s_wave = s_off + kMaxE + 1;
+      publish_routes(logits, T, E, NS, k, gating, renorm, ids_out, w_out, offsets_out, sp_out,
+                     ps_out, s_ids, s_w, s_cnt, s_off, s_wave);
+    }
+    return;
+  }
+  s_tab[tid] = pair_table_entry(tid);
+  route_expert(logits, T, E, k, y, s_rank, s_tok, s_prow, &s_m);
+  const int m = s_m;
+  if (m == 0) return;
+  const int ex = y < E ? y : E;
+  const int NBH = H >> 5, NBF = F >> 5;
+  const int nsteps = (NBH >> 1) / S;
+  const uint32_t rowb = (uint32_t)NBH * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(bank + (int64_t)ex * stride, 2u * F * rowb);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xhl, (uint32_t)T * (uint32_t)H * 4u);
+
+  // the pieces this thread copies: weight piece p = tid + 256 i is 16-byte piece j of stage
+  // row rr = p / PPR; stage row rr = 32 w + 16 t + c is column c of wave w's gate (t = 0) or
+  // up (t = 1) tile; wave w takes FFN block 2 blockIdx.x + w / 2, half w % 2, and column c is
+  // FFN row 32 block + 8 half + (c % 8) + 16 (c / 8) (a row and the row 16 above it, one
+  // code-byte pair of h, in lanes c and c + 8)
+  uint32_t boff[NIB];
+  int bdst[NIB];
+#pragma unroll
+  for (int i = 0; i < NIB; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int pp = p < NPB ? p : NPB - 1;
+    const int rr = pp / PPR, j = pp - rr * PPR;
+    const int w = rr >> 5, t = (rr >> 4) & 1, c = rr & 15;
+    const uint32_t f = 32 * (2 * blockIdx.x + (w >> 1)) + 8 * (w & 1) + (c & 7) + 16 * (c >> 3);
+    boff[i] = (t ? F + f : f) * rowb + 16u * j;
+    bdst[i] = p < NPB ? 16 * p : -1;
+  }
+  // activation piece p = tid + 256 i: piece j of token row i_t = p / PPA (zeros past m)
+  uint32_t aoff[NIA];
+  int adst[NIA];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int it = p / PPA, j = p - it * PPA;
+    aoff[i] = it < m ? (uint32_t)s_tok[it] * (uint32_t)NBH * 128u + 16u * j : kOob;
+    adst[i] = SB + it * AROW + 16 * j;
+  }
+  u32x4_t rb[2][NIB], ra[2][NIA];
+  auto issue = [&](int slot, int st) __attribute__((always_inline)) {
+    st = st < nsteps ? st : nsteps - 1;          // past the end: the last step again, unused
+#pragma unroll
+    for (int i = 0; i < NIB; ++i)
+      rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
+#pragma unroll
+    for (int i = 0; i < NIA; ++i)
+      ra[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 256u * S * st),
+                                                          0, 0);
+  };
+  auto stage_write = [&](int slot) __attribute__((always_inline)) {
+    uint8_t* sb = s_mem + slot * STG;
+#pragma unroll
+    for (int i = 0; i < NIB; ++i)
+      if (bdst[i] >= 0) *reinterpret_cast<u32x4_t*>(sb + bdst[i]) = rb[slot][i];
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) *reinterpret_cast<u32x4_t*>(sb + adst[i]) = ra[slot][i];
+  };
+
+  const int c16 = lane & 15, q = lane >> 4;
+  f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* sb = s_mem + slot * STG;
+    const uint8_t* sa = sb + SB + c16 * AROW + 16 * q;
+#pragma unroll
+    for (int b = 0; b < S; ++b) {
+      const bf16x8_t ah[2] = {*reinterpret_cast<const bf16x8_t*>(sa + 256 * b),
+                              *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128)};
+      const bf16x8_t al[2] = {*reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64),
+                              *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 192)};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t* rw =
+            reinterpret_cast<const uint32_t*>(sb + (32 * wave + 16 * t + c16) * 36 * S + 36 * b);
+        tile_pair_lds(rw, q, ah, al, s_tab, acc[t]);
+      }
+    }
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int st = 0; st < nsteps; st += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 0 || st + 1 < nsteps) {
+        stage_write(u);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(u, st + u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        compute(u);
+      }
+    }
+  }
+
+  // h = silu(g) * u; lane c16 < 8 takes the row 16 above from lane c16 + 8 and writes the
+  // (hi, lo) pair dwords of both rows
+  const int kbf = 2 * blockIdx.x + (wave >> 1);
+  const int j = 8 * (wave & 1) + c16;              // pair index inside the FFN block (c16 < 8)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float hv = silu(acc[0][r]) * acc[1][r];
+    const float hu = dpp_f<0x128>(hv);             // row_ror:8: the value of lane c16 ^ 8
+    const int i = 4 * q + r;
+    if (c16 < 8 && i < m) {
+      uint32_t hi, lo;
+      split_pair(hv, hu, hi, lo);
+      uint32_t* dst = hhl + ((size_t)s_prow[i] * NBF + kbf) * 32 + j;
+      dst[0] = hi;
+      dst[16] = lo;
+    }
+  }
+}
+
+// ---- down + combine --------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(kBdDownWaves * 64) bdec_down_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ hhl,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const float* __restrict__ w, int T, int H, int F, int E, int S, int k,
+    const float* residual, float* y) {
+  constexpr int NW = kBdDownWaves;
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_sp[kDecodeMaxTokens * kBdMaxK];
+  __shared__ float s_w[kDecodeMaxTokens * kBdMaxK];
+  __shared__ int s_act[kMaxE];
+  __shared__ int s_nact;
+  __shared__ float s_o[kDecodeMaxTokens * (kBdMaxK + 1) * 16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int P = T * k, NBIN = E + S;
+  const int NBF = F >> 5;
+  const int r0 = (int)blockIdx.x * 16;
+  if (tid < 256) s_tab[tid] = pair_table_entry(tid);
+  for (int i = tid; i <= NBIN; i += NW * 64) s_off[i] = offsets[i];
+  for (int i = tid; i < P; i += NW * 64) {
+    s_sp[i] = sorted_pairs[i];
+    s_w[i] = w[i];
+  }
+  __syncthreads();
+  // experts with slots: the shared expert first, then the routed ones in index order
+  if (wave == 0) {
+    int seen = 0;
+    if (S > 0) {
+      if (lane == 0) s_act[0] = E;
+      seen = 1;
+    }
+    for (int base = 0; base < E; base += 64) {
+      const int b = base + lane;
+      const bool ne = b < E && s_off[b + 1] > s_off[b];
+      const uint64_t mask = __ballot(ne);
+      if (ne) s_act[seen + __popcll(mask & ((1ull << lane) - 1))] = b;
+      seen += __popcll(mask);
+    }
+    if (lane == 0) s_nact = seen;
+  }
+  __syncthreads();
+  const int nact = s_nact;
+  const int n_my = wave < nact ? (nact - wave + NW - 1) / NW : 0;   // experts wave, wave + NW, ..
+  const int c16 = lane & 15, q = lane >> 4;
+  const int NP = NBF >> 1;
+  const int total = n_my * NP;
+
+  if (total > 0) {
+    const int64_t rowb = (int64_t)NBF * kBlockBytes;
+    const int64_t down_off = 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+    const __amdgpu_buffer_rsrc_t hrs =
+        make_rsrc(hhl, (uint32_t)(P + T * S) * (uint32_t)F * 4u);
+    // the slot row of lane c16 in expert ex (or none)
+    auto prow_of = [&](int ex, int i) __attribute__((always_inline)) {
+      const int sa = s_off[ex], m = s_off[ex + 1] - sa;
+      return i < m ? (sa + i < P ? s_sp[sa + i] : sa + i) : -1;
+    };
+    // issue state: the next block pair to load
+    int i_ei = 0, i_bp = 0;
+    __amdgpu_buffer_rsrc_t i_rs;
+    uint32_t i_aoff = kOob;
+    const uint32_t i_row = (uint32_t)(r0 + c16) * (uint32_t)rowb + 4u * q;
+    auto set_issue = [&](int ei) __attribute__((always_inline)) {
+      const int ex = __builtin_amdgcn_readfirstlane(s_act[wave + NW * ei]);
+      i_rs = make_rsrc(bank + (int64_t)ex * stride + down_off, (uint32_t)(H * rowb));
+      const int pr = prow_of(ex, c16);
+      i_aoff = pr >= 0 ? (uint32_t)pr * (uint32_t)NBF * 128u + 16u * q : kOob;
+    };
+    set_issue(0);
+    uint32_t wr[D][4];
+    u32x4_t ar[D][4];
+    auto issue = [&](int u) __attribute__((always_inline)) {
+      load_bpair(i_rs, i_row + 36u * i_bp, wr[u]);
+      load_apair(hrs, i_aoff, i_bp, ar[u]);
+      if (i_bp + 1 < NP) {
+        ++i_bp;
+      } else if (i_ei + 1 < n_my) {
+        ++i_ei;
+        i_bp = 0;
+        set_issue(i_ei);
+      }                                          // past the last item: it is loaded again
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      issue(u);
+      __builtin_amdgcn_sched_barrier(0);    // the slots are issued in order
+    }
+    int c_ei = 0, c_bp = 0;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i0 = 0; i0 < total; i0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const bool valid = i0 + u < total;
+        {
+          const bf16x8_t ah[2] = {__builtin_bit_cast(bf16x8_t, ar[u][0]),
+                                  __builtin_bit_cast(bf16x8_t, ar[u][2])};
+          const bf16x8_t al[2] = {__builtin_bit_cast(bf16x8_t, ar[u][1]),
+                                  __builtin_bit_cast(bf16x8_t, ar[u][3])};
+          tile_pair(wr[u], ah, al, s_tab, c16, valid, acc);
+        }
+        if (valid && ++c_bp == NP) {
+            const int ex = s_act[wave + NW * c_ei];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int pr = prow_of(ex, 4 * q + r);
+              if (pr >= 0) s_o[pr * 16 + c16] = acc[r];
+            }
+            acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            c_bp = 0;
+            ++c_ei;
+        }
+        issue(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // combine in fixed order: routed j = 0..k-1, then the shared expert, then the residual
+  if (tid < T * 16) {
+    const int t = tid >> 4, c = tid & 15;
+    float a = 0.0f;
+    for (int j = 0; j < k; ++j) a = fmaf(s_w[t * k + j], s_o[(t * k + j) * 16 + c], a);
+    for (int sidx = 0; sidx < S; ++sidx) a += s_o[(P + sidx * T + t) * 16 + c];
+    const int64_t o = (int64_t)t * H + r0 + c;
+    if (residual) a += residual[o];
+    y[o] = a;
+  }
+}
+
+// ---- host side -------------------------------------------------------------------------
+
+bool bdecode_supported(const Shape& sh, int T) {
+  return T >= 1 && T <= kDecodeMaxTokens && sh.k <= kBdMaxK && sh.E + sh.S <= kMaxE &&
+         sh.S <= 1 && sh.H % 64 == 0 && sh.F % 64 == 0;
+}
+
+hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t stride,
+                                const float* wr, const float* bias, const float* x, int T,
+                                float eps, const float* residual, float* y, DecodeScratch sc,
+                                int stages, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!bdecode_supported(sh, T)) return hipErrorInvalidValue;
+  uint32_t* xhl = reinterpret_cast<uint32_t*>(sc.xn);
+  uint32_t* hhl = reinterpret_cast<uint32_t*>(sc.h);
+  hipError_t err;
+  if (stages & 1) {
+    err = launch_router_rows(sh, x, wr, bias, T, eps, sc.logits, nullptr, s, nullptr, xhl);
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 2) {
+    // two tiles a wave (128 FFN rows a workgroup) when that still gives every CU a few
+    // workgroups a routed expert's worth of rows
+    if ((sh.H / 64) % 4 == 0) {
+      const dim3 grid(sh.F / 64, sh.E + sh.S + 1);
+      hipLaunchKernelGGL((bdec_gateup2_kernel<4>), grid, dim3(kBdThreads), 0, s, bank, stride,
+                         xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
+                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl);
+    } else {
+      const int wg_rows = 64 * 1;
+      const dim3 grid((sh.F + wg_rows - 1) / wg_rows, sh.E + sh.S + 1);
+      hipLaunchKernelGGL((bdec_gateup_kernel<1, 4>), grid, dim3(kBdThreads), 0, s, bank, stride,
+                         xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
+                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl);
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 4) {
+    hipLaunchKernelGGL((bdec_down_kernel<4>), dim3(sh.H / 16), dim3(kBdDownWaves * 64), 0, s,
+                       bank, stride, hhl, sc.offsets, sc.sorted_pairs, sc.w, T, sh.H, sh.F,
+                       sh.E, sh.S, sh.k, residual, y);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

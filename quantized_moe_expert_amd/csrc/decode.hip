@@ -38,7 +38,7 @@ template <int EPW, int KM, int TG>
 __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int H, int E, float eps, int use_norm, float* __restrict__ logits,
-    float* __restrict__ rscale, float* __restrict__ xn) {
+    float* __restrict__ rscale, float* __restrict__ xn, uint32_t* __restrict__ xhl) {
   __shared__ float s_red[4][(EPW + 1) * kDecMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * EPW;
@@ -51,6 +51,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
     logits += (size_t)t0 * E;
     if (rscale) rscale += t0;
     if (xn) xn += (size_t)t0 * H;
+    if (xhl) xhl += (size_t)t0 * H;
   }
   float acc[EPW][kDecMaxT], ss[kDecMaxT];
 #pragma unroll
@@ -131,6 +132,28 @@ __global__ void __launch_bounds__(kDecThreads) decode_router_kernel(
       }
       logits[(size_t)t * E + e] = r * dot + (bias ? bias[e] : 0.0f);
       if (use_norm && rscale && blockIdx.x == 0 && q == 0) rscale[t] = r;
+    }
+  }
+  // optional rows of x * r split into bf16 (hi, lo) pairs in code-byte order: per block of 32,
+  // dword j < 16 = (hi(x_j), hi(x_{j+16})), dword 16 + j the lo parts; workgroup b writes
+  // token rows b, b + grid, ...
+  if (xhl) {
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+      float r = 1.0f;
+      if (use_norm) {
+        const int i = EPW * kDecMaxT + t;
+        const float sq = (s_red[0][i] + s_red[1][i]) + (s_red[2][i] + s_red[3][i]);
+        r = 1.0f / sqrtf(sq / (float)H + eps);
+      }
+      const float* src = x + (size_t)t * H;
+      uint32_t* dst = xhl + (size_t)t * H;
+      for (int pi = tid; pi < (H >> 1); pi += kDecThreads) {
+        const int kb = pi >> 4, j = pi & 15;
+        uint32_t hi, lo;
+        split_pair(src[kb * 32 + j] * r, src[kb * 32 + 16 + j] * r, hi, lo);
+        dst[kb * 32 + j] = hi;
+        dst[kb * 32 + 16 + j] = lo;
+      }
     }
   }
   // optional normalised rows: workgroup b writes token rows b, b + grid, ... (same r)
@@ -627,34 +650,34 @@ static bool dispatch_down(DecGeom gm, hipStream_t s, const uint8_t* bank, int64_
 template <int EPW, int KM>
 static void launch_router(dim3 grid, hipStream_t s, const float* x, const float* wr,
                           const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
-                          float* logits, float* rscale, float* xn) {
+                          float* logits, float* rscale, float* xn, uint32_t* xhl) {
   constexpr int kTg = EPW * KM >= 16 ? 1 : (EPW * KM >= 8 ? 2 : 4);
   const int tpg = (T + (int)grid.y - 1) / (int)grid.y;
   if (tpg <= 2 || kTg == 1)
     hipLaunchKernelGGL((decode_router_kernel<EPW, KM, 1>), dim3(grid), dim3(kDecThreads), 0, s,
-                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn);
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn, xhl);
   else
     hipLaunchKernelGGL((decode_router_kernel<EPW, KM, kTg>), dim3(grid), dim3(kDecThreads), 0, s,
-                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn);
+                       x, wr, bias, T, sh.H, sh.E, e_arg, use_norm, logits, rscale, xn, xhl);
 }
 
 template <int EPW>
 static bool dispatch_router(int km, dim3 grid, hipStream_t s, const float* x, const float* wr,
                             const float* bias, int T, const Shape& sh, float e_arg, int use_norm,
-                            float* logits, float* rscale, float* xn) {
+                            float* logits, float* rscale, float* xn, uint32_t* xhl) {
   switch (km) {
-    case 1: launch_router<EPW, 1>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
-    case 2: launch_router<EPW, 2>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
-    case 3: case 4: launch_router<EPW, 4>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
-    case 5: case 6: case 7: launch_router<EPW, 7>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
-    case 8: launch_router<EPW, 8>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn); return true;
+    case 1: launch_router<EPW, 1>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl); return true;
+    case 2: launch_router<EPW, 2>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl); return true;
+    case 3: case 4: launch_router<EPW, 4>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl); return true;
+    case 5: case 6: case 7: launch_router<EPW, 7>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl); return true;
+    case 8: launch_router<EPW, 8>(grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl); return true;
   }
   return false;
 }
 
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,
-                              float* rscale, hipStream_t s, float* xn) {
+                              float* rscale, hipStream_t s, float* xn, uint32_t* xhl) {
   // experts a workgroup: at least 256 workgroups where the expert count allows
   const int epw = sh.E >= 256 ? 1 : (sh.E >= 128 ? 2 : 1);
   const int use_norm = eps >= 0.0f ? 1 : 0;
@@ -664,9 +687,9 @@ hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
   const dim3 grid((sh.E + epw - 1) / epw, T > 4 ? (T + 3) / 4 : 1);
   bool ok;
   if (epw == 2)
-    ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
+    ok = dispatch_router<2>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl);
   else
-    ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn);
+    ok = dispatch_router<1>(km, grid, s, x, wr, bias, T, sh, e_arg, use_norm, logits, rscale, xn, xhl);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -678,30 +701,10 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   if (T == 0) return hipSuccess;
   const int use_norm = eps >= 0.0f ? 1 : 0;
   hipError_t err = hipSuccess;
-  if (T > kDecodeFusedMaxT) {
-    // several tokens: route once (rows normalised into xn), then the slot-chunked GEMVs
-    if (stages & 1) {
-      // logits of the normalised rows (r * <x, w_e> + b_e) and the rows themselves, then
-      // top-k and the permutation in one workgroup
-      err = launch_router_rows(sh, x, wr, bias, T, use_norm ? eps : -1.0f, sc.logits, nullptr, s,
-                               use_norm ? sc.xn : nullptr);
-      if (err != hipSuccess) return err;
-      err = launch_topk_permute(sh, sc.logits, T, sc.ids, sc.w, sc.offsets, sc.sorted_pairs,
-                                sc.pair_slot, sc.count, s);
-      if (err != hipSuccess) return err;
-    }
-    const float* xin = use_norm ? sc.xn : x;
-    if (stages & 2) {
-      err = launch_gemv(sh, 0, bank, stride, sc.offsets, sc.sorted_pairs, xin, sc.h, T, s);
-      if (err != hipSuccess) return err;
-    }
-    if (stages & 4) {
-      err = launch_gemv(sh, 1, bank, stride, sc.offsets, nullptr, sc.h, sc.o, T, s);
-      if (err != hipSuccess) return err;
-      err = launch_combine(sh, sc.o, sc.pair_slot, sc.w, T, residual, y, s);
-    }
-    return err;
-  }
+  // more tokens, or every slot's h too large for the down workgroup's LDS: the batched
+  // kernels (bdecode.hip), also three launches
+  if (T > kDecodeFusedMaxT || !decode_down_fused_fits(sh, T))
+    return launch_bdecode_layer(sh, bank, stride, wr, bias, x, T, eps, residual, y, sc, stages, s);
   if (stages & 1) {
     err = launch_router_rows(sh, x, wr, bias, T, eps, sc.logits, sc.rscale, s);
     if (err != hipSuccess) return err;
@@ -748,17 +751,12 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   }
   if (!(stages & 4)) return hipSuccess;
 
-  // down + combine (fused when every slot's h fits in LDS)
-  if (decode_down_fused_fits(sh, T)) {
-    const DecGeom dn = dec_geom(sh.F / 32);
-    if (!dispatch_down(dn, s, bank, stride, sc.h, sc.offsets, sc.pair_slot, sc.w, T, sh,
-                       residual, y))
-      return hipErrorInvalidValue;
-    return hipGetLastError();
-  }
-  err = launch_gemv(sh, 1, bank, stride, sc.offsets, nullptr, sc.h, sc.o, T, s);
-  if (err != hipSuccess) return err;
-  return launch_combine(sh, sc.o, sc.pair_slot, sc.w, T, residual, y, s);
+  // down + combine
+  const DecGeom dn = dec_geom(sh.F / 32);
+  if (!dispatch_down(dn, s, bank, stride, sc.h, sc.offsets, sc.pair_slot, sc.w, T, sh, residual,
+                     y))
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -53,25 +53,28 @@ struct DecodeScratch {
   int32_t* sorted_pairs;  // [T * k]
   int32_t* pair_slot;     // [T * k]
   float* h;               // [rows, F]
-  float* o;               // [rows, H] (only when down + combine are separate launches)
-  float* xn;              // [T, H] normalised input (batches above kDecodeFusedMaxT)
+  float* xn;              // [T, H]: the batched kernels' pre-split input rows
   int32_t* count;         // sanitised-pair count of the permutation
 };
 
 constexpr int kDecodeMaxTokens = 16;
-// Up to this many tokens a decode layer routes inside its gate/up workgroups (three
-// launches); above it the route, permutation, GEMVs and combine are separate launches.
+// Up to this many tokens a decode layer runs the dequant-GEMV kernels of decode.hip; above it
+// the batched kernels of bdecode.hip (matrix cores).  Both take three launches a layer.
 constexpr int kDecodeFusedMaxT = 4;
 // logits (and, with eps >= 0, the RMSNorm scale of each row into rscale and the normalised
-// rows into xn, where those are non-null) for T <= 16 rows
+// rows into xn, where those are non-null; with xhl non-null, the rows times their scale as
+// bf16 (hi, lo) pairs in code-byte order) for T <= 16 rows
 hipError_t launch_router_rows(const Shape& sh, const float* x, const float* wr,
                               const float* bias, int T, float eps, float* logits,
-                              float* rscale, hipStream_t s, float* xn = nullptr);
-// top-k of T complete logit rows and the permutation of the resulting route table; one
-// workgroup when T * E logits fit its LDS, else launch_topk + launch_permute
-hipError_t launch_topk_permute(const Shape& sh, const float* logits, int T, int32_t* ids,
-                               float* w, int32_t* offsets, int32_t* sorted_pairs,
-                               int32_t* pair_slot, int32_t* invalid_count, hipStream_t s);
+                              float* rscale, hipStream_t s, float* xn = nullptr,
+                              uint32_t* xhl = nullptr);
+// The batched decode layer (bdecode.hip): sc.xn holds the pre-split input rows and sc.h the
+// pre-split h rows in pair order; no o buffer.
+bool bdecode_supported(const Shape& sh, int T);
+hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t stride,
+                                const float* wr, const float* bias, const float* x, int T,
+                                float eps, const float* residual, float* y, DecodeScratch sc,
+                                int stages, hipStream_t s);
 bool decode_down_fused_fits(const Shape& sh, int T);
 hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t stride,
                                const float* wr, const float* bias, const float* x, int T,

@@ -108,36 +108,6 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(
   if (tid == 0) *invalid_count = s_bad;
 }
 
-// Decode batches: top-k of T logit rows (one wave a row, from LDS) and the permutation of the
-// route table they make, in one workgroup.  Top-k ids are in range, so nothing is sanitised.
-__global__ void __launch_bounds__(1024) topk_permute_kernel(
-    const float* __restrict__ logits, int T, int k, int E, int S, int gating, int renorm,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_slot,
-    int32_t* __restrict__ invalid_count) {
-  extern __shared__ float s_l[];             // T x E logits
-  __shared__ int s_id[kSmallThreads];
-  __shared__ float s_w[kSmallThreads];
-  __shared__ int s_cnt[kSmallThreads];
-  __shared__ int s_off[kSmallThreads + 1];
-  __shared__ int s_wave[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int P = T * k;
-  for (int t = wave; t < T; t += kSmallThreads / 64) {
-    for (int e = lane; e < E; e += 64) s_l[t * E + e] = logits[(size_t)t * E + e];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
-    wave_topk(s_l + t * E, E, k, gating, renorm, s_id + t * k, s_w + t * k);
-  }
-  __syncthreads();
-  if (tid < P) {
-    ids[tid] = s_id[tid];
-    w[tid] = s_w[tid];
-  }
-  permute_small_core(s_id, P, T, E, S, s_cnt, s_off, s_wave, offsets, sorted_pairs, pair_slot);
-  if (tid == 0) *invalid_count = 0;
-}
-
 // Pass 1: sanitise, per-block histogram -> counts[blk * E + e]; invalid count per block.
 __global__ void __launch_bounds__(kPairsPerBlock) permute_count_kernel(
     int32_t* __restrict__ ids, float* __restrict__ w, int P, int E,
@@ -272,23 +242,6 @@ hipError_t launch_permute(const Shape& sh, int32_t* ids, float* w, int T, const 
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_kernel, dim3(rows, (sh.H / 4 + 255) / 256), dim3(256), 0, s, x,
                      sorted_pairs, T, sh.k, sh.H, x_perm_bf16, x_perm);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_permute(const Shape& sh, const float* logits, int T, int32_t* ids,
-                               float* w, int32_t* offsets, int32_t* sorted_pairs,
-                               int32_t* pair_slot, int32_t* invalid_count, hipStream_t s) {
-  const size_t lds = (size_t)T * sh.E * sizeof(float);
-  if (T == 0) return hipSuccess;
-  if (!use_small(sh, T) || lds > 32 * 1024) {
-    hipError_t e = launch_topk(sh, logits, T, ids, w, s);
-    if (e != hipSuccess) return e;
-    return launch_permute(sh, ids, w, T, nullptr, nullptr, 0, offsets, sorted_pairs, pair_slot,
-                          invalid_count, nullptr, s);
-  }
-  hipLaunchKernelGGL(topk_permute_kernel, dim3(1), dim3(kSmallThreads), lds, s, logits, T, sh.k,
-                     sh.E, sh.S, sh.gating, sh.renorm, ids, w, offsets, sorted_pairs, pair_slot,
-                     invalid_count);
   return hipGetLastError();
 }
 

@@ -19,8 +19,16 @@ BUILD = os.path.join(ROOT, "_build")
 OUT = os.path.join(BUILD, "asan")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/lib/llvm/bin/clang++"
-OTHERS = ("quant.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip", "combine.hip",
-          "decode.hip")
+def _others():
+    """Every source of the library but api.hip, as the build lists them."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from quantized_moe_expert_amd import build
+    srcs = build.LIBS[os.path.join(build.PKG, "libmoe_iq4nl.so")]
+    return tuple(os.path.basename(f) for f in srcs if os.path.basename(f) != "api.hip")
+
+
+OTHERS = _others()
 HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 

@@ -258,16 +258,19 @@ def test_invalid_routes_contribute_nothing():
     assert_close(buf.y.cpu().numpy(), ref, REL_L2_GEMV, "invalid routes")
 
 
-@pytest.mark.parametrize("name,lift", [("xing4_decode", (20, 40)), ("qwen3next_like", (3, 500, 77)),
-                                       ("tiny", (5,))])
-def test_one_token_decode_with_exact_logit_ties(name, lift):
+@pytest.mark.parametrize("name,lift,T", [("xing4_decode", (20, 40), 1),
+                                         ("qwen3next_like", (3, 500, 77), 1), ("tiny", (5,), 1),
+                                         ("xing4_decode", (20, 40), 16),
+                                         ("qwen3next_like", (3, 500, 77), 9),
+                                         ("dsv41_like", (383, 0), 16)])
+def test_decode_with_exact_logit_ties(name, lift, T):
     """Every expert gets the same router row, so all logits tie except the lifted experts'
     (bias +1): the top-k set is the lifted experts plus the lowest-index tied ones.  The
-    routed workgroups of the one-token path pick their experts by set membership, the
-    publishing one by the full top-k; both must agree with the oracle's tie rule."""
+    routed workgroups of the one-token path pick their experts by set membership, those of
+    the batched path by counting the experts ranked above theirs, the publishing one by the
+    full top-k; all must agree with the oracle's tie rule."""
     wl = WORKLOADS[name]
     s = wl.shape
-    T = 1
     wr_h = np.repeat(G.router_weight(wl, 0)[:1], s.n_experts, axis=0)
     bias_h = np.zeros(s.n_experts, np.float32)
     for e in lift:
@@ -282,6 +285,7 @@ def test_one_token_decode_with_exact_logit_ties(name, lift):
     xh = G.activations(wl, T)
     ref, parts = oracle_layer(wl, 0, xh, return_parts=True, bias=bias_h, w_router=wr_h)
     want = sorted(lift) + [e for e in range(s.n_experts) if e not in lift][:s.top_k - len(lift)]
-    assert sorted(parts["ids"][0].tolist()) == sorted(want)
+    for t in range(T):
+        assert sorted(parts["ids"][t].tolist()) == sorted(want)
     assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
-    assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"ties {name}")
+    assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"ties {name} T={T}")
