@@ -147,7 +147,8 @@ __device__ void publish_routes(const float* __restrict__ logits, int T, int E, i
   const int P = T * k, NBIN = E + S;
   for (int i = tid; i < NBIN; i += kBdThreads) s_cnt[i] = 0;
   for (int t = wave; t < T; t += kBdThreads / 64)
-    wave_topk(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k, s_w + t * k);
+    wave_topk_one_layout(logits + (size_t)t * E, E, k, gating, renorm, s_ids + t * k,
+                         s_w + t * k);
   __syncthreads();
   for (int p = tid; p < P; p += kBdThreads) atomicAdd(&s_cnt[s_ids[p]], 1);
   if (tid < S) s_cnt[E + tid] = T;
@@ -359,21 +360,24 @@ __global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
 
 // Workgroup-cooperative variant: the 4 waves take 64 FFN rows (a gate and an up tile each) and
 // walk K in steps of S block pairs together.  Each step's weights (128 rows x 36 S bytes) and
-// activations (up to 16 token rows x 2 S blocks x 128 bytes) are fetched as whole 16-byte
+// activations (up to 16 token rows x 2 S blocks x 128 bytes) are fetched as whole PB-byte
 // pieces of contiguous memory by all 256 threads, two steps ahead into registers, then written
 // to one of two LDS stages; one barrier a step; the waves read their operands from LDS.  Every
 // cache line of the weights is then read by one instruction, where the direct variant above
-// reads 20 bytes of each of 16 rows an instruction.  Needs rows of a multiple of 16 bytes and
-// whole steps (H / 64 a multiple of S, S a multiple of 4).
-template <int S>
-__global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
+// reads 20 bytes of each of 16 rows an instruction.  Needs rows of a multiple of PB bytes and
+// whole steps (H / 64 a multiple of S).  At most three waves a SIMD: the schedule the compiler
+// makes in that register budget measured faster than with four (or two).
+template <int S, int PB>
+__global__ void __launch_bounds__(kBdThreads) __attribute__((amdgpu_waves_per_eu(1, 3)))
+bdec_gateup2_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ xhl,
     const float* __restrict__ logits, int T, int H, int F, int E, int NS, int k, int gating,
     int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
     int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl) {
-  static_assert(S % 4 == 0, "16-byte pieces of a step need S a multiple of 4");
-  constexpr int PPR = 9 * S / 4;                   // 16-byte pieces of a weight row a step
+  static_assert((PB == 16 || PB == 8) && (36 * S) % PB == 0, "whole weight pieces a step");
+  typedef uint32_t piece_t __attribute__((ext_vector_type(PB / 4)));
+  constexpr int PPR = 36 * S / PB;                 // weight pieces of a row a step
   constexpr int NPB = 128 * PPR;                   // weight pieces a step
   constexpr int NIB = (NPB + kBdThreads - 1) / kBdThreads;
   constexpr int PPA = 16 * S;                      // 16-byte pieces of a token row a step
@@ -385,8 +389,11 @@ __global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
   constexpr int STG = SB + kDecodeMaxTokens * AROW;
   static_assert(2 * STG >= (int)(2 * kDecodeMaxTokens * kBdMaxK * 4 + 2 * (kMaxE + 1) * 4 + 16),
                 "the route-table workgroup's arrays share the stage memory");
-  __shared__ __align__(16) uint8_t s_mem[2 * STG];
-  __shared__ uint32_t s_tab[256];
+  // the pair table first (LDS address 0: a lookup address is the code byte times 4), then the
+  // two stages
+  __shared__ __align__(16) uint8_t s_mem[1024 + 2 * STG];
+  uint32_t* s_tab = reinterpret_cast<uint32_t*>(s_mem);
+  uint8_t* s_stg = s_mem + 1024;
   __shared__ int s_rank[kDecodeMaxTokens];
   __shared__ int s_tok[kDecodeMaxTokens];
   __shared__ int s_prow[kDecodeMaxTokens];
@@ -397,7 +404,7 @@ __global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
   const int y = blockIdx.y;
   if (y == E + NS) {                      // the route-table workgroup (grid column 0 only)
     if (blockIdx.x == 0) {
-      int* s_ids = reinterpret_cast<int*>(s_mem);
+      int* s_ids = reinterpret_cast<int*>(s_stg);
       float* s_w = reinterpret_cast<float*>(s_ids + kDecodeMaxTokens * kBdMaxK);
       int* s_cnt = reinterpret_cast<int*>(s_w + kDecodeMaxTokens * kBdMaxK);
       int* s_off = s_cnt + kMaxE + 1;
@@ -432,8 +439,8 @@ __global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
     const int rr = pp / PPR, j = pp - rr * PPR;
     const int w = rr >> 5, t = (rr >> 4) & 1, c = rr & 15;
     const uint32_t f = 32 * (2 * blockIdx.x + (w >> 1)) + 8 * (w & 1) + (c & 7) + 16 * (c >> 3);
-    boff[i] = (t ? F + f : f) * rowb + 16u * j;
-    bdst[i] = p < NPB ? 16 * p : -1;
+    boff[i] = (t ? F + f : f) * rowb + (uint32_t)PB * j;
+    bdst[i] = p < NPB ? PB * p : -1;
   }
   // activation piece p = tid + 256 i: piece j of token row i_t = p / PPA (zeros past m)
   uint32_t aoff[NIA];
@@ -445,37 +452,53 @@ __global__ void __launch_bounds__(kBdThreads, 2) bdec_gateup2_kernel(
     aoff[i] = it < m ? (uint32_t)s_tok[it] * (uint32_t)NBH * 128u + 16u * j : kOob;
     adst[i] = SB + it * AROW + 16 * j;
   }
-  u32x4_t rb[2][NIB], ra[2][NIA];
+  piece_t rb[2][NIB];
+  u32x4_t ra[2][NIA];
   auto issue = [&](int slot, int st) __attribute__((always_inline)) {
     st = st < nsteps ? st : nsteps - 1;          // past the end: the last step again, unused
 #pragma unroll
-    for (int i = 0; i < NIB; ++i)
-      rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
+    for (int i = 0; i < NIB; ++i) {
+      if constexpr (PB == 16)
+        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
+      else
+        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)boff[i], 36 * S * st, 0);
+    }
 #pragma unroll
     for (int i = 0; i < NIA; ++i)
       ra[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 256u * S * st),
                                                           0, 0);
   };
   auto stage_write = [&](int slot) __attribute__((always_inline)) {
-    uint8_t* sb = s_mem + slot * STG;
+    uint8_t* sb = s_stg + slot * STG;
 #pragma unroll
     for (int i = 0; i < NIB; ++i)
-      if (bdst[i] >= 0) *reinterpret_cast<u32x4_t*>(sb + bdst[i]) = rb[slot][i];
+      if (bdst[i] >= 0) *reinterpret_cast<piece_t*>(sb + bdst[i]) = rb[slot][i];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) *reinterpret_cast<u32x4_t*>(sb + adst[i]) = ra[slot][i];
   };
 
   const int c16 = lane & 15, q = lane >> 4;
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  // activation fragments of rows past the expert's tokens are never read (their products
+  // land in rows of the result that are not stored): zero once, and left alone
+  bf16x8_t ah[2], al[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ah[i] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    al[i] = ah[i];
+  }
+  const bool arow = c16 < m;
   auto compute = [&](int slot) __attribute__((always_inline)) {
-    const uint8_t* sb = s_mem + slot * STG;
+    const uint8_t* sb = s_stg + slot * STG;
     const uint8_t* sa = sb + SB + c16 * AROW + 16 * q;
 #pragma unroll
     for (int b = 0; b < S; ++b) {
-      const bf16x8_t ah[2] = {*reinterpret_cast<const bf16x8_t*>(sa + 256 * b),
-                              *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128)};
-      const bf16x8_t al[2] = {*reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64),
-                              *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 192)};
+      if (arow) {
+        ah[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b);
+        ah[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128);
+        al[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64);
+        al[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 192);
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t* rw =
@@ -680,9 +703,9 @@ hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t st
   if (stages & 2) {
     // two tiles a wave (128 FFN rows a workgroup) when that still gives every CU a few
     // workgroups a routed expert's worth of rows
-    if ((sh.H / 64) % 4 == 0) {
+    if ((sh.H / 64) % 2 == 0) {
       const dim3 grid(sh.F / 64, sh.E + sh.S + 1);
-      hipLaunchKernelGGL((bdec_gateup2_kernel<4>), grid, dim3(kBdThreads), 0, s, bank, stride,
+      hipLaunchKernelGGL((bdec_gateup2_kernel<2, 8>), grid, dim3(kBdThreads), 0, s, bank, stride,
                          xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
                          sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl);
     } else {

@@ -140,17 +140,11 @@ __device__ __forceinline__ int wave_topk_member_any(const float* __restrict__ l,
   return wave_topk_member<16>(l, E, k, target);
 }
 
-// ids[0..k-1], w[0..k-1] of one token's logits l[0..E-1] (E <= 1024, k <= 32); all 64
-// lanes of the wave take part; lanes j < k write entry j.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int k, int gating,
-                                          int renorm, int32_t* ids, float* w) {
+// Gating weights of the selection my_e (lane j < k holds the j-th selected expert) and the
+// writes of ids[j], w[j].
+__device__ __forceinline__ void wave_gate(const float* __restrict__ l, int E, int k, int gating,
+                                          int renorm, int my_e, int32_t* ids, float* w) {
   const int lane = threadIdx.x & 63;
-  int my_e;
-  if (E <= 64) my_e = wave_select<1>(l, E, k);
-  else if (E <= 128) my_e = wave_select<2>(l, E, k);
-  else if (E <= 256) my_e = wave_select<4>(l, E, k);
-  else if (E <= 512) my_e = wave_select<8>(l, E, k);
-  else my_e = wave_select<16>(l, E, k);
   const bool mine = lane < k;
   const float v = mine ? l[my_e] : 0.0f;
   float s;
@@ -173,6 +167,27 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, in
     ids[lane] = my_e;
     w[lane] = s;
   }
+}
+
+// ids[0..k-1], w[0..k-1] of one token's logits l[0..E-1] (E <= 1024, k <= 32); all 64
+// lanes of the wave take part; lanes j < k write entry j.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int k, int gating,
+                                          int renorm, int32_t* ids, float* w) {
+  int my_e;
+  if (E <= 64) my_e = wave_select<1>(l, E, k);
+  else if (E <= 128) my_e = wave_select<2>(l, E, k);
+  else if (E <= 256) my_e = wave_select<4>(l, E, k);
+  else if (E <= 512) my_e = wave_select<8>(l, E, k);
+  else my_e = wave_select<16>(l, E, k);
+  wave_gate(l, E, k, gating, renorm, my_e, ids, w);
+}
+
+// wave_topk with the one lane layout of 16 logits a lane (any E <= 1024): a single code path,
+// for kernels where the five layouts' code would raise the register count of the whole kernel.
+__device__ __forceinline__ void wave_topk_one_layout(const float* __restrict__ l, int E, int k,
+                                                     int gating, int renorm, int32_t* ids,
+                                                     float* w) {
+  wave_gate(l, E, k, gating, renorm, wave_select<16>(l, E, k), ids, w);
 }
 
 }  // namespace moe
