@@ -101,14 +101,15 @@ __device__ __forceinline__ void tile_pair(const uint32_t (&w)[4], const bf16x8_t
   for (int r = 0; r < 4; ++r) acc[r] = fmaf(d1, p1[r], fmaf(d0, p0[r], acc[r]));
 }
 
-// tile_pair with the block pair's 9 dwords in LDS at rw (the weights staged by the
-// workgroup): dwords q, q + 1 (the even block's code bytes 4q..4q+3 straddle them), 5 + q
-// (the odd block's), and the scales in dwords 0 (low half) and 4 (high half).
+// tile_pair with the block pair's 9 dwords in LDS at rw (the weights staged in LDS): dwords
+// q, q + 1 (the even block's code bytes 4q..4q+3 straddle them), 5 + q (the odd block's), and
+// the scales in dwords 0 (low half) and 4 (high half).
 __device__ __forceinline__ void tile_pair_lds(const uint32_t* rw, int q, const bf16x8_t (&ah)[2],
                                               const bf16x8_t (&al)[2], const uint32_t* s_tab,
-                                              f32x4_t& acc) {
+                                              f32x4_t& acc, bool keep = true) {
   const uint32_t w0 = rw[q], w1 = rw[q + 1], w3 = rw[5 + q];
-  const uint32_t dd = __builtin_amdgcn_perm(rw[4], rw[0], 0x07060100u);
+  uint32_t dd = __builtin_amdgcn_perm(rw[4], rw[0], 0x07060100u);
+  dd = keep ? dd : 0u;
   const float d0 = __half2float(__ushort_as_half((unsigned short)(dd & 0xFFFFu)));
   const float d1 = __half2float(__ushort_as_half((unsigned short)(dd >> 16)));
   const bf16x8_t b0 = b_pairs(__builtin_amdgcn_alignbit(w1, w0, 16), s_tab);
@@ -680,6 +681,167 @@ __global__ void __launch_bounds__(kBdDownWaves * 64) bdec_down_kernel(
   }
 }
 
+// Staged variant of the down kernel: a wave's 16 rows of its expert are fetched SD block pairs
+// at a time as 8-byte pieces of contiguous row segments (36 SD bytes a row; a load instruction
+// covers several whole segments instead of 20 bytes of each of 16 rows), two steps ahead into
+// registers, and written to the wave's own LDS stage right before its operands are read
+// (one wave writes and reads it: its LDS accesses complete in order, no barrier).  The
+// activations (h rows) are loaded as in the direct variant.  Rows of an even number of block
+// pairs (F a multiple of 128).
+template <int SD>
+__global__ void __launch_bounds__(kBdDownWaves * 64) bdec_down2_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ hhl,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const float* __restrict__ w, int T, int H, int F, int E, int S, int k,
+    const float* residual, float* y) {
+  constexpr int NW = kBdDownWaves;
+  constexpr int PPR = 36 * SD / 8;                 // 8-byte pieces of a row a step
+  constexpr int NPD = 16 * PPR;                    // pieces a step (16 rows)
+  constexpr int NID = (NPD + 63) / 64;             // load instructions a step
+  __shared__ uint32_t s_tab[256];
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_sp[kDecodeMaxTokens * kBdMaxK];
+  __shared__ float s_w[kDecodeMaxTokens * kBdMaxK];
+  __shared__ int s_act[kMaxE];
+  __shared__ int s_nact;
+  __shared__ float s_o[kDecodeMaxTokens * (kBdMaxK + 1) * 16];
+  __shared__ __align__(16) uint8_t s_wst[NW][NPD * 8];   // each wave's weight stage
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int P = T * k, NBIN = E + S;
+  const int NBF = F >> 5;
+  const int r0 = (int)blockIdx.x * 16;
+  if (tid < 256) s_tab[tid] = pair_table_entry(tid);
+  for (int i = tid; i <= NBIN; i += NW * 64) s_off[i] = offsets[i];
+  for (int i = tid; i < P; i += NW * 64) {
+    s_sp[i] = sorted_pairs[i];
+    s_w[i] = w[i];
+  }
+  __syncthreads();
+  // experts with slots: the shared expert first, then the routed ones in index order
+  if (wave == 0) {
+    int seen = 0;
+    if (S > 0) {
+      if (lane == 0) s_act[0] = E;
+      seen = 1;
+    }
+    for (int base = 0; base < E; base += 64) {
+      const int b = base + lane;
+      const bool ne = b < E && s_off[b + 1] > s_off[b];
+      const uint64_t mask = __ballot(ne);
+      if (ne) s_act[seen + __popcll(mask & ((1ull << lane) - 1))] = b;
+      seen += __popcll(mask);
+    }
+    if (lane == 0) s_nact = seen;
+  }
+  __syncthreads();
+  const int nact = s_nact;
+  const int n_my = wave < nact ? (nact - wave + NW - 1) / NW : 0;   // experts wave, wave + NW, ..
+  const int c16 = lane & 15, q = lane >> 4;
+  const int nst = (NBF >> 1) / SD;                 // steps an expert
+  const int total = n_my * nst;
+
+  if (total > 0) {
+    const uint32_t rowb = (uint32_t)NBF * kBlockBytes;
+    const int64_t down_off = 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+    const __amdgpu_buffer_rsrc_t hrs =
+        make_rsrc(hhl, (uint32_t)(P + T * S) * (uint32_t)F * 4u);
+    auto prow_of = [&](int ex, int i) __attribute__((always_inline)) {
+      const int sa = s_off[ex], m = s_off[ex + 1] - sa;
+      return i < m ? (sa + i < P ? s_sp[sa + i] : sa + i) : -1;
+    };
+    // this lane's pieces: piece p = lane + 64 i is 8-byte piece j of row r = p / PPR
+    uint32_t poff[NID];
+    int pdst[NID];
+#pragma unroll
+    for (int i = 0; i < NID; ++i) {
+      const int p = lane + 64 * i;
+      const int pp = p < NPD ? p : NPD - 1;
+      const int r = pp / PPR, j = pp - r * PPR;
+      poff[i] = (uint32_t)(r0 + r) * rowb + 8u * j;
+      pdst[i] = p < NPD ? 8 * p : -1;
+    }
+    uint8_t* stg = s_wst[wave];
+    // issue state: the next step to load
+    int i_ei = 0, i_st = 0;
+    __amdgpu_buffer_rsrc_t i_rs;
+    uint32_t i_aoff = kOob;
+    auto set_issue = [&](int ei) __attribute__((always_inline)) {
+      const int ex = __builtin_amdgcn_readfirstlane(s_act[wave + NW * ei]);
+      i_rs = make_rsrc(bank + (int64_t)ex * stride + down_off, (uint32_t)H * rowb);
+      const int pr = prow_of(ex, c16);
+      i_aoff = pr >= 0 ? (uint32_t)pr * (uint32_t)NBF * 128u + 16u * q : kOob;
+    };
+    set_issue(0);
+    u32x2_t wb[2][NID];
+    u32x4_t ar[2][SD][4];
+    auto issue = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NID; ++i)
+        wb[u][i] = __builtin_amdgcn_raw_buffer_load_b64(i_rs, (int)poff[i], 36 * SD * i_st, 0);
+#pragma unroll
+      for (int b = 0; b < SD; ++b) load_apair(hrs, i_aoff, SD * i_st + b, ar[u][b]);
+      if (i_st + 1 < nst) {
+        ++i_st;
+      } else if (i_ei + 1 < n_my) {
+        ++i_ei;
+        i_st = 0;
+        set_issue(i_ei);
+      }                                          // past the last item: it is loaded again
+    };
+    issue(0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1);
+    __builtin_amdgcn_sched_barrier(0);
+    int c_ei = 0, c_st = 0;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i0 = 0; i0 < total; i0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool valid = i0 + u < total;
+#pragma unroll
+        for (int i = 0; i < NID; ++i)
+          if (pdst[i] >= 0) *reinterpret_cast<u32x2_t*>(stg + pdst[i]) = wb[u][i];
+#pragma unroll
+        for (int b = 0; b < SD; ++b) {
+          const bf16x8_t ah[2] = {__builtin_bit_cast(bf16x8_t, ar[u][b][0]),
+                                  __builtin_bit_cast(bf16x8_t, ar[u][b][2])};
+          const bf16x8_t al[2] = {__builtin_bit_cast(bf16x8_t, ar[u][b][1]),
+                                  __builtin_bit_cast(bf16x8_t, ar[u][b][3])};
+          const uint32_t* rw = reinterpret_cast<const uint32_t*>(stg + c16 * 36 * SD + 36 * b);
+          tile_pair_lds(rw, q, ah, al, s_tab, acc, valid);
+        }
+        if (valid && ++c_st == nst) {
+          const int ex = s_act[wave + NW * c_ei];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int pr = prow_of(ex, 4 * q + r);
+            if (pr >= 0) s_o[pr * 16 + c16] = acc[r];
+          }
+          acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          c_st = 0;
+          ++c_ei;
+        }
+        issue(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // combine in fixed order: routed j = 0..k-1, then the shared expert, then the residual
+  if (tid < T * 16) {
+    const int t = tid >> 4, c = tid & 15;
+    float a = 0.0f;
+    for (int j = 0; j < k; ++j) a = fmaf(s_w[t * k + j], s_o[(t * k + j) * 16 + c], a);
+    for (int sidx = 0; sidx < S; ++sidx) a += s_o[(P + sidx * T + t) * 16 + c];
+    const int64_t o = (int64_t)t * H + r0 + c;
+    if (residual) a += residual[o];
+    y[o] = a;
+  }
+}
+
 // ---- host side -------------------------------------------------------------------------
 
 bool bdecode_supported(const Shape& sh, int T) {
@@ -719,9 +881,14 @@ hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t st
     if (err != hipSuccess) return err;
   }
   if (stages & 4) {
-    hipLaunchKernelGGL((bdec_down_kernel<4>), dim3(sh.H / 16), dim3(kBdDownWaves * 64), 0, s,
-                       bank, stride, hhl, sc.offsets, sc.sorted_pairs, sc.w, T, sh.H, sh.F,
-                       sh.E, sh.S, sh.k, residual, y);
+    if ((sh.F / 64) % 2 == 0)
+      hipLaunchKernelGGL((bdec_down2_kernel<2>), dim3(sh.H / 16), dim3(kBdDownWaves * 64), 0, s,
+                         bank, stride, hhl, sc.offsets, sc.sorted_pairs, sc.w, T, sh.H, sh.F,
+                         sh.E, sh.S, sh.k, residual, y);
+    else
+      hipLaunchKernelGGL((bdec_down_kernel<4>), dim3(sh.H / 16), dim3(kBdDownWaves * 64), 0, s,
+                         bank, stride, hhl, sc.offsets, sc.sorted_pairs, sc.w, T, sh.H, sh.F,
+                         sh.E, sh.S, sh.k, residual, y);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
