@@ -414,7 +414,22 @@ def decode_record(name, wl, d):
         "dominant": {"stage": dom, "bound": "hbm",
                      "frac": round(d[f"{dom}_gbs"] / HBM_PEAK_GBS, 4)},
         "active_experts_per_layer_mean": round(sum(d["U"]) / len(d["U"]), 2),
+        **batched_traffic(wl, d),
     }
+
+
+def batched_traffic(wl, d):
+    """For the batched decode kernels (5 to 16 tokens): their HBM bytes a launch from the
+    profiles/ summary (looked up by grid) next to the algorithmic bytes a launch."""
+    s = wl.shape
+    if d["T"] <= 4:
+        return {}
+    gu_grid = (s.ffn // 64) * (s.n_experts + s.n_shared + 1) * 256
+    dn_grid = (s.hidden // 16) * 512
+    return {"gate_up_traffic_bytes": traffic("bdec_gateup2_kernel<2, 8>", gu_grid),
+            "gate_up_algorithmic_bytes": round(d["gate_up_bytes"]),
+            "down_traffic_bytes": traffic("bdec_down2_kernel<2>", dn_grid),
+            "down_algorithmic_bytes": round(d["down_bytes"])}
 
 
 def prefill_record(name, wl, p):
@@ -562,7 +577,8 @@ def main():
         "roofline": {
             "kernel": ("decode_gateup_kernel (routing + IQ4_NL dequant-GEMV gate/up + SwiGLU)"
                        if d["T"] <= 4 else
-                       "gemv_kernel<..., true> (IQ4_NL dequant-GEMV gate/up + SwiGLU)"),
+                       "bdec_gateup2_kernel (routing + IQ4_NL gate/up on bf16 matrix cores + "
+                       "SwiGLU)"),
             "bound": "hbm",
             "achieved": round(gu_gbs, 1),
             "peak": HBM_PEAK_GBS,

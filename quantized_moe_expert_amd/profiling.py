@@ -26,6 +26,8 @@ KERNEL_SOURCES = {
     "decode_down_combine_kernel": ("decode.hip", "gemv_core.h", "common.h", "kernels.h"),
     "gemm_kernel<true>": ("gemm.hip", "common.h", "kernels.h"),
     "gemm_kernel<false>": ("gemm.hip", "common.h", "kernels.h"),
+    "bdec_gateup2_kernel": ("bdecode.hip", "common.h", "route_core.h", "kernels.h"),
+    "bdec_down2_kernel": ("bdecode.hip", "common.h", "route_core.h", "kernels.h"),
 }
 PMC_FILE = "pmc_traffic_decode_and_prefill_all_workloads.txt"
 
@@ -47,7 +49,7 @@ def stats_summary(stats_csv, command):
     rows = list(csv.DictReader(open(stats_csv)))
     out = [f"command: {command}", "",
            f"{'calls':>7} {'avg us':>10} {'min us':>10} {'max us':>10} {'% time':>7}  kernel"]
-    for r in rows[:16]:
+    for r in rows[:24]:
         out.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                    f"{float(r['Percentage']):7.2f}  {r['Name'][:110]}")
