@@ -711,17 +711,15 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   }
   if (stages & 2) {
 
-  // gate/up with routing.  One token: 4 passes of the least-waste geometry.  Several
-  // tokens: when the row splits exactly into 16 lanes x 7 blocks (hidden 3584), 2 passes of
-  // that geometry (smaller workgroups, so the shared expert's token tiles spread wider).
+  // gate/up with routing: 4 passes of the least-waste geometry (a 16-lane x 7-block geometry
+  // with 2 passes for hidden 3584 at 2-4 tokens measured 1.65x slower)
   const int nb = sh.H / 32;
-  const bool wide = T > 1 && nb == 112;
-  const DecGeom gu = wide ? DecGeom{16, 7} : dec_geom(nb);
+  const DecGeom gu = dec_geom(nb);
   if (gu.lpr == 0) return hipErrorInvalidValue;
   // several tokens over many experts make the in-workgroup routing costly: fewer, larger
   // workgroups (8 passes)
-  const bool heavy = !wide && T > 1 && sh.E >= 256;
-  const int passes = wide ? 2 : (heavy ? 8 : 4);
+  const bool heavy = T > 1 && sh.E >= 256;
+  const int passes = heavy ? 8 : 4;
   const int orows_wg = (kDecThreads / 64) * passes * (64 / gu.lpr) / 2;
   const int max_active = (int)std::min<int64_t>(sh.E, (int64_t)T * sh.k) + sh.S;
   const int tch = T;                               // every token of an expert in one workgroup
@@ -729,11 +727,7 @@ hipError_t launch_decode_layer(const Shape& sh, const uint8_t* bank, int64_t str
   dim3 grid((sh.F + orows_wg - 1) / orows_wg, max_active * ((T + tch - 1) / tch) + 1);
   const float* rs = use_norm ? sc.rscale : nullptr;
   bool ok;
-  if (wide) {
-    launch_up<16, 7, 2, 2>(grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
-                           sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h, tch);
-    ok = true;
-  } else if (heavy && gu.bpl <= 2)
+  if (heavy && gu.bpl <= 2)
     ok = dispatch_up<2, 8>(gu, grid, s, bank, stride, x, rs, sc.logits, T, sh, sc.ids, sc.w,
                            sc.offsets, sc.sorted_pairs, sc.pair_slot, sc.h);
   else if (heavy)
