@@ -14,7 +14,7 @@ import quantized_moe_expert_amd as M
 from quantized_moe_expert_amd import layer as L
 from oracle import moe as omoe
 from synth import generator as G
-from synth.configs import (WORKLOADS, TINY, XING4_DECODE, LayerShape, SIGMOID,
+from synth.configs import (WORKLOADS, TINY, XING4_DECODE, LayerShape, SIGMOID, SOFTMAX,
                            Workload)
 
 from .helpers import (REL_L2_GEMV, REL_L2_MFMA, assert_close, desc_of, oracle_bank,
@@ -147,6 +147,44 @@ def test_fused_decode_layer_odd_row_lengths(name, T):
     xh = omoe.rmsnorm(G.activations(wl, T), 1e-6)
     ref, parts = oracle_layer(wl, 0, xh, return_parts=True)
     assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
+    assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"{name} T={T}")
+
+
+# degenerate routes: no shared expert; one expert that every token picks; k = E (every
+# expert picked by every token); softmax gating without renormalisation
+EDGE_SHAPES = {
+    "no_shared": Workload(name="no_shared", cfg_id=9,
+                          shape=LayerShape(hidden=512, ffn=256, n_experts=16, top_k=4, n_shared=0,
+                                           gating=SIGMOID, renormalize=1), layers=1),
+    "one_expert": Workload(name="one_expert", cfg_id=10,
+                           shape=LayerShape(hidden=256, ffn=128, n_experts=1, top_k=1,
+                                            n_shared=0, gating=SIGMOID, renormalize=1), layers=1),
+    "k_equals_e": Workload(name="k_equals_e", cfg_id=11,
+                           shape=LayerShape(hidden=256, ffn=192, n_experts=4, top_k=4, n_shared=1,
+                                            gating=SOFTMAX, renormalize=0), layers=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_SHAPES))
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_fused_decode_degenerate_routes(name, T):
+    """Both decode paths (T = 1: dequant-GEMV; T = 5, 16: matrix cores) on routes with no
+    shared expert, a single expert, or k = E; ids bit-exact, y against the oracle, and the
+    split stages bit-identical to one call."""
+    wl = EDGE_SHAPES[name]
+    bank_t, bank = L.make_bank(wl, 0)
+    wr, bias = L.make_router(wl, 0)
+    x = L.make_activations(wl, T)
+    buf = L.LayerBuffers(wl.shape, T)
+    y = L.decode_layer_fused(buf, x, wr, bias, bank).clone()
+    y3 = torch.empty_like(y)
+    for st in (M.MOE_DECODE_ROUTER, M.MOE_DECODE_GATE_UP, M.MOE_DECODE_DOWN):
+        L.decode_layer_fused(buf, x, wr, bias, bank, out=y3, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y)
+    ref, parts = oracle_layer(wl, 0, G.activations(wl, T), return_parts=True)
+    assert np.array_equal(buf.ids.cpu().numpy(), parts["ids"])
+    assert_close(buf.w.cpu().numpy(), parts["weights"], 1e-5, f"weights {name} T={T}")
     assert_close(y.cpu().numpy(), ref, REL_L2_GEMV, f"{name} T={T}")
 
 
