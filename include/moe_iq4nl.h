@@ -187,8 +187,8 @@ moe_status moe_combine(const moe_desc *desc, const float *o, const int32_t *pair
                        const float *topk_w, int32_t n_tokens, const float *residual,
                        float *y, hipStream_t stream);
 
-/* Fused decode layer for small batches (1 <= T <= 16): three launches for T <= 4, separate
- * route / permute / GEMV / combine launches for 4 < T <= 16, no host round trip
+/* Fused decode layer for small batches (1 <= T <= 16): three launches (router, gate/up, down
+ * with the combine) at every T, no host round trip
  * (PocketLLM page, "Known limitations": decode bound by launch count; Red Lite "1. The idea":
  * a whole token routed on the GPU).  Computes
  *   xn = norm_eps >= 0 ? x / sqrt(mean(x^2) + norm_eps) : x        (per row)
@@ -197,13 +197,14 @@ moe_status moe_combine(const moe_desc *desc, const float *o, const int32_t *pair
  * GEMV arithmetic of moe_expert_gemv_iq4nl and the fixed-order combine of moe_combine.
  *   x [T, H], residual [T, H], y [T, H] fp32; y may alias x and residual.
  *   topk_ids [T, k], topk_w [T, k]: optional outputs of the route table (NULL: kept in ws).
- * stages: bitmask of the parts to enqueue -- MOE_DECODE_ROUTER (logits; for T > 4 also the
- * RMSNorm, top-k and permutation), MOE_DECODE_GATE_UP (gate/up; for T <= 4 with the routing
- * redone in every workgroup), MOE_DECODE_DOWN (down + combine); MOE_DECODE_ALL for the layer.
+ * stages: bitmask of the parts to enqueue -- MOE_DECODE_ROUTER (RMSNorm and logits),
+ * MOE_DECODE_GATE_UP (gate/up, the routing redone in every workgroup, and the route table
+ * and permutation), MOE_DECODE_DOWN (down + combine); MOE_DECODE_ALL for the layer.
  * Split calls must be enqueued in that order on one stream with the same arguments and
  * workspace.
  * ws: at least moe_workspace_size(desc, T) bytes, 256-byte aligned; holds the logits, the
- * permutation and h.  The route table never leaves the device between the launches. */
+ * permutation, h, the per-slot down outputs and the down's row-range counters (set by the
+ * gate/up launch).  The route table never leaves the device between the launches. */
 #define MOE_DECODE_ROUTER 1
 #define MOE_DECODE_GATE_UP 2
 #define MOE_DECODE_DOWN 4

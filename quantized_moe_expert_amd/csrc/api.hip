@@ -100,11 +100,11 @@ Shape shape_of(const moe_desc* d) {
 size_t logits_bytes(const moe_desc* d, int32_t T) { return align256((size_t)T * d->n_experts * 4); }
 
 // Fused decode layer: header | logits | rscale | ids | w | offsets | sorted_pairs | pair_slot |
-// h | xn.  For the batched kernels (above kDecodeFusedMaxT tokens, or when the down stage's
+// h | xn | o | done.  For the batched kernels (above kDecodeFusedMaxT tokens, or when the down stage's
 // LDS cannot hold every slot's h) xn and h hold bf16 (hi, lo) pair rows: the same bytes as
 // fp32 rows.
 struct DecodeLayout {
-  size_t logits, rscale, ids, w, offsets, sp, ps, h, xn, total;
+  size_t logits, rscale, ids, w, offsets, sp, ps, h, xn, o, done, total;
 };
 
 DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
@@ -121,6 +121,8 @@ DecodeLayout decode_layout(const moe_desc* d, int32_t T) {
   L.ps = off; off += align256(P * 4);
   L.h = off; off += align256(rows * d->ffn * 4);
   L.xn = off; off += align256((size_t)T * d->hidden * 4);
+  L.o = off; off += align256(rows * d->hidden * 4);
+  L.done = off; off += align256((size_t)(d->hidden / 128 + 1) * 4);
   L.total = off;
   return L;
 }
@@ -338,6 +340,8 @@ moe_status run_decode_layer(const moe_desc* desc, const moe_bank* bank, const fl
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
   sc.xn = reinterpret_cast<float*>(b + L.xn);
+  sc.o = reinterpret_cast<float*>(b + L.o);
+  sc.done = reinterpret_cast<int32_t*>(b + L.done);
   sc.count = reinterpret_cast<int32_t*>(b);
   return hip_status(moe::launch_decode_layer(shape_of(desc), bank->base, bank->expert_stride,
                                              w_router, bias, x, n_tokens, norm_eps, residual, y,
@@ -411,6 +415,8 @@ moe_status moe_decode_chain(const moe_desc* desc, const moe_layer* layers, int32
   sc.pair_slot = reinterpret_cast<int32_t*>(b + L.ps);
   sc.h = reinterpret_cast<float*>(b + L.h);
   sc.xn = reinterpret_cast<float*>(b + L.xn);
+  sc.o = reinterpret_cast<float*>(b + L.o);
+  sc.done = reinterpret_cast<int32_t*>(b + L.done);
   sc.count = reinterpret_cast<int32_t*>(b);
   for (int32_t l = 0; l < n_layers; ++l) {
     sc.ids = topk_ids ? topk_ids + l * P : reinterpret_cast<int32_t*>(b + L.ids);

@@ -8,16 +8,19 @@
 //
 //   router  (decode_router_kernel, decode.hip): the logits of the T tokens, and each token's row
 //           scaled by its RMSNorm factor and split into bf16 (hi, lo) pairs in code-byte order.
-//   gate/up (bdec_gateup_kernel): one workgroup per (expert, 64 or 128 FFN rows).  It finds the
+//   gate/up (bdec_gateup2_kernel): one workgroup per (expert, 64 FFN rows).  It finds the
 //           tokens that picked its expert by counting, for each token, the experts ranked above
 //           the expert (fewer than k: picked, and that count is its place j in the token's
 //           list), so no workgroup waits for another.  h leaves as bf16 (hi, lo) pairs in pair
 //           order (row t * k + j; the shared expert's rows after the P routed ones).  The grid's
 //           last row holds one workgroup that runs the full top-k, the gating weights, the
 //           route table and the permutation.
-//   down    (bdec_down_kernel): one workgroup per 16 output rows over every active expert; o
-//           of every slot for those rows stays in LDS and the combine (fixed order: routed
-//           j = 0..k-1, the shared expert, the residual) writes y.
+//   down    (bdec_down3_kernel): one workgroup per (expert, 128 output rows), the K loop of the
+//           gate/up kernel; o of every slot goes to the workspace, and the workgroup that
+//           completes a row range (a counter per range) combines it in fixed order (routed
+//           j = 0..k-1, the shared expert, the residual) into y.  Shapes whose rows do not fit
+//           it take bdec_down2_kernel / bdec_down_kernel: one workgroup per 16 output rows over
+//           every active expert, o in LDS.
 //
 // Matrix products.  An expert's tokens (at most 16: a token picks an expert once) are the 16
 // rows of the A operand and 16 weight rows the columns of B.  One instruction covers one IQ4_NL
@@ -49,6 +52,11 @@ constexpr int kBdMaxK = 32;
 constexpr uint32_t kOob = 0x80000000u; // buffer offset past every range: the load returns 0
 constexpr int kNt = 0;                  // cache policy of the weight loads: default (a 128-byte
                                         // line is read by several instructions: it must stay)
+constexpr int kSc1 = 16;                // cache policy bit sc1: device-coherent loads and stores
+// Copies of the pair table in the cooperative kernels' LDS: lane l looks up in copy l % kTabRep,
+// stored interleaved (entry e of copy g at dword kTabRep e + g), so that the lanes of one copy
+// share a few banks that no other copy uses and random code bytes collide in fewer banks.
+constexpr int kTabRep = 16;
 
 // Buffer resource over `bytes` bytes from `base`; loads past the end return zeros and touch no
 // memory (the rows of A past an expert's tokens).
@@ -78,6 +86,17 @@ __device__ __forceinline__ bf16x8_t b_pairs(uint32_t cw, const uint32_t* s_tab) 
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// b_pairs in the interleaved copies: tabl = the pair table's copies + this lane's copy.
+template <int R>
+__device__ __forceinline__ bf16x8_t b_pairs_rep(uint32_t cw, const uint32_t* tabl) {
+  u32x4_t v;
+  v[0] = tabl[(cw & 0xFFu) * R];
+  v[1] = tabl[((cw >> 8) & 0xFFu) * R];
+  v[2] = tabl[((cw >> 16) & 0xFFu) * R];
+  v[3] = tabl[(cw >> 24) * R];
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // acc += d_even * (A_even . B_even) + d_odd * (A_odd . B_odd) for one block pair of one tile of
 // 16 weight rows; ah / al: the hi and lo activation fragments of the two blocks.  keep = false
 // (a block pair past the end, loaded again so that no branch surrounds the loads) zeroes both
@@ -103,7 +122,9 @@ __device__ __forceinline__ void tile_pair(const uint32_t (&w)[4], const bf16x8_t
 
 // tile_pair with the block pair's 9 dwords in LDS at rw (the weights staged in LDS): dwords
 // q, q + 1 (the even block's code bytes 4q..4q+3 straddle them), 5 + q (the odd block's), and
-// the scales in dwords 0 (low half) and 4 (high half).
+// the scales in dwords 0 (low half) and 4 (high half).  s_tab: the pair table, or with R > 1
+// this lane's copy of R interleaved ones (b_pairs_rep).
+template <int R = 1>
 __device__ __forceinline__ void tile_pair_lds(const uint32_t* rw, int q, const bf16x8_t (&ah)[2],
                                               const bf16x8_t (&al)[2], const uint32_t* s_tab,
                                               f32x4_t& acc, bool keep = true) {
@@ -112,8 +133,8 @@ __device__ __forceinline__ void tile_pair_lds(const uint32_t* rw, int q, const b
   dd = keep ? dd : 0u;
   const float d0 = __half2float(__ushort_as_half((unsigned short)(dd & 0xFFFFu)));
   const float d1 = __half2float(__ushort_as_half((unsigned short)(dd >> 16)));
-  const bf16x8_t b0 = b_pairs(__builtin_amdgcn_alignbit(w1, w0, 16), s_tab);
-  const bf16x8_t b1 = b_pairs(w3, s_tab);
+  const bf16x8_t b0 = b_pairs_rep<R>(__builtin_amdgcn_alignbit(w1, w0, 16), s_tab);
+  const bf16x8_t b1 = b_pairs_rep<R>(w3, s_tab);
   const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
   f32x4_t p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[0], b0, z, 0, 0, 0);
   p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[0], b0, p0, 0, 0, 0);
@@ -133,6 +154,123 @@ __device__ __forceinline__ void load_apair(__amdgpu_buffer_rsrc_t rs, uint32_t a
   a[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 64u), 0, 0);
   a[2] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 128u), 0, 0);
   a[3] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(o + 192u), 0, 0);
+}
+
+// kTabRep interleaved copies of the pair table (entry e of copy g at dword kTabRep e + g), by the
+// 256 threads of a workgroup.
+__device__ __forceinline__ void fill_tab_rep(uint32_t* s_tab) {
+  for (int i = threadIdx.x; i < 256 * kTabRep; i += kBdThreads)
+    s_tab[i] = pair_table_entry(i / kTabRep);
+}
+
+// A cooperative workgroup's stage: the weights of 128 rows x S block pairs (36 S bytes a row),
+// then up to 16 activation rows of 2 S blocks (128 bytes a block: 16 hi pair dwords, then 16
+// lo), each row padded by 16 bytes so that the 16 rows of a fragment read hit distinct banks.
+// Weights arrive as PB-byte pieces, activations as 16-byte pieces, every thread taking
+// pieces tid, tid + 256, ...
+template <int S, int PB>
+struct Stage {
+  static_assert((PB == 16 || PB == 8) && (36 * S) % PB == 0, "whole weight pieces a step");
+  static constexpr int PPR = 36 * S / PB;                  // weight pieces of a row a step
+  static constexpr int NPB = 128 * PPR;                    // weight pieces a step
+  static constexpr int NIB = (NPB + kBdThreads - 1) / kBdThreads;
+  static constexpr int PPA = 16 * S;                       // activation pieces of a row a step
+  static constexpr int NIA = kDecodeMaxTokens * PPA / kBdThreads;
+  static constexpr int SB = 128 * 36 * S;                  // weight bytes of a stage
+  static constexpr int AROW = 256 * S + 16;                // bytes of an activation row
+  static constexpr int STG = SB + kDecodeMaxTokens * AROW; // bytes of a stage
+};
+
+// The K loop of a cooperative workgroup (4 waves): every step's pieces are fetched two steps
+// ahead into registers, written to one of two LDS stages, one barrier a step, and wave w then
+// multiplies stage rows 32 w + 16 t + (0..15) (tile t = 0, 1) by the m activation rows into
+// acc[t] (the matrix instruction's result layout: lane l holds column l % 16, rows
+// 4 (l / 16) .. + 3).  boff / bdst: this thread's weight pieces (byte offset in wrs at step 0;
+// byte offset in the stage, or -1 for none); aoff / adst: its activation pieces (kOob past the
+// m rows: zeros).  A step advances the weight offsets by 36 S bytes and the activation offsets
+// by 256 S.  s_stg: two stages of Stage<S, PB>::STG bytes; s_tab: kTabRep interleaved copies of
+// the pair table (fill_tab_rep).
+template <int S, int PB>
+__device__ __forceinline__ void staged_kloop(
+    __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t xrs,
+    const uint32_t (&boff)[Stage<S, PB>::NIB], const int (&bdst)[Stage<S, PB>::NIB],
+    const uint32_t (&aoff)[Stage<S, PB>::NIA], const int (&adst)[Stage<S, PB>::NIA], int nsteps,
+    int m, int wave, int lane, uint8_t* s_stg, const uint32_t* s_tab, f32x4_t (&acc)[2]) {
+  using G = Stage<S, PB>;
+  typedef uint32_t piece_t __attribute__((ext_vector_type(PB / 4)));
+  piece_t rb[2][G::NIB];
+  u32x4_t ra[2][G::NIA];
+  auto issue = [&](int slot, int st) __attribute__((always_inline)) {
+    st = st < nsteps ? st : nsteps - 1;          // past the end: the last step again, unused
+#pragma unroll
+    for (int i = 0; i < G::NIB; ++i) {
+      if constexpr (PB == 16)
+        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
+      else
+        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)boff[i], 36 * S * st, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < G::NIA; ++i)
+      ra[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 256u * S * st),
+                                                          0, 0);
+  };
+  auto stage_write = [&](int slot) __attribute__((always_inline)) {
+    uint8_t* sb = s_stg + slot * G::STG;
+#pragma unroll
+    for (int i = 0; i < G::NIB; ++i)
+      if (bdst[i] >= 0) *reinterpret_cast<piece_t*>(sb + bdst[i]) = rb[slot][i];
+#pragma unroll
+    for (int i = 0; i < G::NIA; ++i) *reinterpret_cast<u32x4_t*>(sb + adst[i]) = ra[slot][i];
+  };
+
+  const int c16 = lane & 15, q = lane >> 4;
+  // activation fragments of rows past the m rows are never read (their products land in
+  // rows of the result that are not stored): zero once, and left alone
+  bf16x8_t ah[2], al[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ah[i] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    al[i] = ah[i];
+  }
+  const bool arow = c16 < m;
+  const uint32_t* tabl = s_tab + (lane % kTabRep);
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* sb = s_stg + slot * G::STG;
+    const uint8_t* sa = sb + G::SB + c16 * G::AROW + 16 * q;
+#pragma unroll
+    for (int b = 0; b < S; ++b) {
+      if (arow) {
+        ah[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b);
+        ah[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128);
+        al[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64);
+        al[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 192);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t* rw =
+            reinterpret_cast<const uint32_t*>(sb + (32 * wave + 16 * t + c16) * 36 * S + 36 * b);
+        tile_pair_lds<kTabRep>(rw, q, ah, al, tabl, acc[t]);
+      }
+    }
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int st = 0; st < nsteps; st += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 0 || st + 1 < nsteps) {
+        stage_write(u);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(u, st + u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        compute(u);
+      }
+    }
+  }
 }
 
 // The route table of T tokens by one workgroup of 256 threads: top-k and gating weights of
@@ -252,7 +390,7 @@ __global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
     const float* __restrict__ logits, int T, int H, int F, int E, int S, int k, int gating,
     int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
-    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl) {
+    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl, int32_t* __restrict__ done) {
   __shared__ uint32_t s_tab[256];
   __shared__ int s_rank[kDecodeMaxTokens];
   __shared__ int s_tok[kDecodeMaxTokens];
@@ -272,6 +410,7 @@ __global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
     if (blockIdx.x == 0)
       publish_routes(logits, T, E, S, k, gating, renorm, ids_out, w_out, offsets_out, sp_out,
                      ps_out, s_ids, s_w, s_cnt, s_off, s_wave);
+      for (int i = tid; i < (H >> 7); i += kBdThreads) done[i] = 0;   // the down's counters
     return;
   }
   s_tab[tid] = pair_table_entry(tid);
@@ -375,26 +514,17 @@ bdec_gateup2_kernel(
     const float* __restrict__ logits, int T, int H, int F, int E, int NS, int k, int gating,
     int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
-    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl) {
-  static_assert((PB == 16 || PB == 8) && (36 * S) % PB == 0, "whole weight pieces a step");
-  typedef uint32_t piece_t __attribute__((ext_vector_type(PB / 4)));
-  constexpr int PPR = 36 * S / PB;                 // weight pieces of a row a step
-  constexpr int NPB = 128 * PPR;                   // weight pieces a step
-  constexpr int NIB = (NPB + kBdThreads - 1) / kBdThreads;
-  constexpr int PPA = 16 * S;                      // 16-byte pieces of a token row a step
-  constexpr int NIA = kDecodeMaxTokens * PPA / kBdThreads;
-  constexpr int SB = 128 * 36 * S;                 // weight stage bytes
-  constexpr int AROW = 256 * S + 16;               // token row of an activation stage (padded:
-                                                   // the 16 rows of a fragment read hit
-                                                   // distinct banks)
-  constexpr int STG = SB + kDecodeMaxTokens * AROW;
+    int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl, int32_t* __restrict__ done) {
+  using G = Stage<S, PB>;
+  constexpr int PPR = G::PPR, NPB = G::NPB, NIB = G::NIB, PPA = G::PPA, NIA = G::NIA;
+  constexpr int SB = G::SB, AROW = G::AROW, STG = G::STG;
   static_assert(2 * STG >= (int)(2 * kDecodeMaxTokens * kBdMaxK * 4 + 2 * (kMaxE + 1) * 4 + 16),
                 "the route-table workgroup's arrays share the stage memory");
   // the pair table first (LDS address 0: a lookup address is the code byte times 4), then the
   // two stages
-  __shared__ __align__(16) uint8_t s_mem[1024 + 2 * STG];
+  __shared__ __align__(16) uint8_t s_mem[1024 * kTabRep + 2 * STG];
   uint32_t* s_tab = reinterpret_cast<uint32_t*>(s_mem);
-  uint8_t* s_stg = s_mem + 1024;
+  uint8_t* s_stg = s_mem + 1024 * kTabRep;
   __shared__ int s_rank[kDecodeMaxTokens];
   __shared__ int s_tok[kDecodeMaxTokens];
   __shared__ int s_prow[kDecodeMaxTokens];
@@ -412,10 +542,11 @@ bdec_gateup2_kernel(
       int* s_wave = s_off + kMaxE + 1;
       publish_routes(logits, T, E, NS, k, gating, renorm, ids_out, w_out, offsets_out, sp_out,
                      ps_out, s_ids, s_w, s_cnt, s_off, s_wave);
+      for (int i = tid; i < (H >> 7); i += kBdThreads) done[i] = 0;   // the down's counters
     }
     return;
   }
-  s_tab[tid] = pair_table_entry(tid);
+  fill_tab_rep(s_tab);
   route_expert(logits, T, E, k, y, s_rank, s_tok, s_prow, &s_m);
   const int m = s_m;
   if (m == 0) return;
@@ -453,79 +584,10 @@ bdec_gateup2_kernel(
     aoff[i] = it < m ? (uint32_t)s_tok[it] * (uint32_t)NBH * 128u + 16u * j : kOob;
     adst[i] = SB + it * AROW + 16 * j;
   }
-  piece_t rb[2][NIB];
-  u32x4_t ra[2][NIA];
-  auto issue = [&](int slot, int st) __attribute__((always_inline)) {
-    st = st < nsteps ? st : nsteps - 1;          // past the end: the last step again, unused
-#pragma unroll
-    for (int i = 0; i < NIB; ++i) {
-      if constexpr (PB == 16)
-        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
-      else
-        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)boff[i], 36 * S * st, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NIA; ++i)
-      ra[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 256u * S * st),
-                                                          0, 0);
-  };
-  auto stage_write = [&](int slot) __attribute__((always_inline)) {
-    uint8_t* sb = s_stg + slot * STG;
-#pragma unroll
-    for (int i = 0; i < NIB; ++i)
-      if (bdst[i] >= 0) *reinterpret_cast<piece_t*>(sb + bdst[i]) = rb[slot][i];
-#pragma unroll
-    for (int i = 0; i < NIA; ++i) *reinterpret_cast<u32x4_t*>(sb + adst[i]) = ra[slot][i];
-  };
-
-  const int c16 = lane & 15, q = lane >> 4;
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  // activation fragments of rows past the expert's tokens are never read (their products
-  // land in rows of the result that are not stored): zero once, and left alone
-  bf16x8_t ah[2], al[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    ah[i] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
-    al[i] = ah[i];
-  }
-  const bool arow = c16 < m;
-  auto compute = [&](int slot) __attribute__((always_inline)) {
-    const uint8_t* sb = s_stg + slot * STG;
-    const uint8_t* sa = sb + SB + c16 * AROW + 16 * q;
-#pragma unroll
-    for (int b = 0; b < S; ++b) {
-      if (arow) {
-        ah[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b);
-        ah[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128);
-        al[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64);
-        al[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 192);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t* rw =
-            reinterpret_cast<const uint32_t*>(sb + (32 * wave + 16 * t + c16) * 36 * S + 36 * b);
-        tile_pair_lds(rw, q, ah, al, s_tab, acc[t]);
-      }
-    }
-  };
-
-  issue(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int st = 0; st < nsteps; st += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u == 0 || st + 1 < nsteps) {
-        stage_write(u);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(u, st + u + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        compute(u);
-      }
-    }
-  }
+  staged_kloop<S, PB>(wrs, xrs, boff, bdst, aoff, adst, nsteps, m, wave, lane, s_stg, s_tab,
+                      acc);
+  const int c16 = lane & 15, q = lane >> 4;
 
   // h = silu(g) * u; lane c16 < 8 takes the row 16 above from lane c16 + 8 and writes the
   // (hi, lo) pair dwords of both rows
@@ -842,6 +904,142 @@ __global__ void __launch_bounds__(kBdDownWaves * 64) bdec_down2_kernel(
   }
 }
 
+// Down by cooperative tiles: one workgroup per (expert, 128 output rows), the K loop of the
+// gate/up kernel over the expert's h rows (A) and its down rows (B).  Each slot's 128 outputs
+// go to o; then the workgroup adds its slot count to the row range's counter in `done`, and
+// the one that brings it to P + T S (every slot of every expert done) combines the range in
+// fixed order (routed j = 0..k-1, the shared expert, the residual) and clears the counter.
+// Every expert's h is then read once a row range, where the per-16-row kernel above reads it
+// once every 16 rows.  Needs H a multiple of 128 and whole steps (F / 64 a multiple of S).
+template <int S, int PB>
+__global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
+    const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ hhl,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const float* __restrict__ w, int T, int H, int F, int E, int NS, int k, float* o,
+    int32_t* __restrict__ done, const float* residual, float* y) {
+  using G = Stage<S, PB>;
+  __shared__ __align__(16) uint8_t s_mem[1024 * kTabRep + 2 * G::STG];
+  uint32_t* s_tab = reinterpret_cast<uint32_t*>(s_mem);
+  uint8_t* s_stg = s_mem + 1024 * kTabRep;
+  __shared__ int s_prow[kDecodeMaxTokens];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ex = blockIdx.y;                       // E: the shared expert
+  const int sa = offsets[ex], m = offsets[ex + 1] - sa;
+  if (m <= 0) return;
+  const int P = T * k, nslots = P + T * NS;
+  fill_tab_rep(s_tab);
+  if (tid < m) s_prow[tid] = sa + tid < P ? sorted_pairs[sa + tid] : sa + tid;
+  __syncthreads();
+  const int NBF = F >> 5;
+  const int nsteps = (NBF >> 1) / S;
+  const uint32_t rowb = (uint32_t)NBF * kBlockBytes;
+  const int r0 = (int)blockIdx.x * 128;
+  const int64_t down_off = 2 * (int64_t)F * ((int64_t)(H >> 5) * kBlockBytes);
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(bank + (int64_t)ex * stride + down_off + (int64_t)r0 * rowb, 128u * rowb);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(hhl, (uint32_t)nslots * (uint32_t)F * 4u);
+
+  // weight piece p = tid + 256 i: piece j of stage row (output row r0 +) rr = p / PPR
+  uint32_t boff[G::NIB];
+  int bdst[G::NIB];
+#pragma unroll
+  for (int i = 0; i < G::NIB; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int pp = p < G::NPB ? p : G::NPB - 1;
+    const int rr = pp / G::PPR, j = pp - rr * G::PPR;
+    boff[i] = (uint32_t)rr * rowb + (uint32_t)PB * j;
+    bdst[i] = p < G::NPB ? PB * p : -1;
+  }
+  // activation piece p = tid + 256 i: piece j of the h row of slot i_t = p / PPA (zeros past m)
+  uint32_t aoff[G::NIA];
+  int adst[G::NIA];
+#pragma unroll
+  for (int i = 0; i < G::NIA; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int it = p / G::PPA, j = p - it * G::PPA;
+    aoff[i] = it < m ? (uint32_t)s_prow[it] * (uint32_t)NBF * 128u + 16u * j : kOob;
+    adst[i] = G::SB + it * G::AROW + 16 * j;
+  }
+  f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  staged_kloop<S, PB>(wrs, xrs, boff, bdst, aoff, adst, nsteps, m, wave, lane, s_stg, s_tab,
+                      acc);
+  // o is stored at the device-coherent level (sc1: as the compiler's device-scope atomic
+  // stores), so no workgroup has to write back its L2 (a device-scope release fence writes back
+  // the XCD's whole L2: one a workgroup made this kernel four times slower).  Each thread waits
+  // until its o stores are complete before the workgroup counts its slots done; the workgroup
+  // that finds every slot done invalidates its stale cached lines (an acquire fence) and only
+  // then reads o.
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(o, (uint32_t)nslots * (uint32_t)H * 4u);
+  const int c16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * q + r;
+      if (i < m)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(acc[t][r]), ors,
+            (int)(((uint32_t)s_prow[i] * H + r0 + 32 * wave + 16 * t + c16) * 4u), 0, kSc1);
+    }
+  __builtin_amdgcn_s_waitcnt(0);                   // this thread's o stores are complete
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&done[blockIdx.x], m, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) + m == nslots;
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop stale cached lines of o
+  // thread (c, u0) = (tid % 128, tid / 128) combines column r0 + c of tokens u0, u0 + 2, ..;
+  // the loads of two routed terms of every token go out together (a few round trips in all)
+  constexpr int NU = kDecodeMaxTokens / 2;
+  const int r = r0 + (tid & 127), u0 = tid >> 7;
+  const __amdgpu_buffer_rsrc_t wrr = make_rsrc(w, (uint32_t)P * 4u);
+  float a[NU], sh[NU], rs[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = u0 + 2 * u;
+    const bool ok = t < T;
+    a[u] = 0.0f;
+    sh[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                ors, ok && NS > 0 ? (int)(((uint32_t)(P + t) * H + r) * 4u) : (int)kOob, 0, kSc1));
+    rs[u] = ok && residual ? residual[(int64_t)t * H + r] : 0.0f;
+  }
+  for (int j0 = 0; j0 < k; j0 += 2) {
+    float v[2][NU], wv[2][NU];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int t = u0 + 2 * u, j = j0 + jj;
+        const bool ok = t < T && j < k;          // else an offset past the end: zero
+        v[jj][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                       ors, ok ? (int)(((uint32_t)(t * k + j) * H + r) * 4u) : (int)kOob, 0,
+                       kSc1));
+        wv[jj][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        wrr, ok ? (t * k + j) * 4 : (int)kOob, 0, 0));
+      }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        if (j0 + jj < k) a[u] = fmaf(wv[jj][u], v[jj][u], a[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int t = u0 + 2 * u;
+    if (t < T) {
+      float b = a[u];
+      if (NS > 0) b += sh[u];
+      if (residual) b += rs[u];
+      y[(int64_t)t * H + r] = b;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&done[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- host side -------------------------------------------------------------------------
 
 bool bdecode_supported(const Shape& sh, int T) {
@@ -869,19 +1067,25 @@ hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t st
       const dim3 grid(sh.F / 64, sh.E + sh.S + 1);
       hipLaunchKernelGGL((bdec_gateup2_kernel<2, 8>), grid, dim3(kBdThreads), 0, s, bank, stride,
                          xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
-                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl);
+                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl,
+                         sc.done);
     } else {
       const int wg_rows = 64 * 1;
       const dim3 grid((sh.F + wg_rows - 1) / wg_rows, sh.E + sh.S + 1);
       hipLaunchKernelGGL((bdec_gateup_kernel<1, 4>), grid, dim3(kBdThreads), 0, s, bank, stride,
                          xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
-                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl);
+                         sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl,
+                         sc.done);
     }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (stages & 4) {
-    if ((sh.F / 64) % 2 == 0)
+    if (sh.H % 128 == 0 && (sh.F / 64) % 2 == 0)
+      hipLaunchKernelGGL((bdec_down3_kernel<2, 8>), dim3(sh.H / 128, sh.E + sh.S),
+                         dim3(kBdThreads), 0, s, bank, stride, hhl, sc.offsets, sc.sorted_pairs,
+                         sc.w, T, sh.H, sh.F, sh.E, sh.S, sh.k, sc.o, sc.done, residual, y);
+    else if ((sh.F / 64) % 2 == 0)
       hipLaunchKernelGGL((bdec_down2_kernel<2>), dim3(sh.H / 16), dim3(kBdDownWaves * 64), 0, s,
                          bank, stride, hhl, sc.offsets, sc.sorted_pairs, sc.w, T, sh.H, sh.F,
                          sh.E, sh.S, sh.k, residual, y);

@@ -54,6 +54,8 @@ struct DecodeScratch {
   int32_t* pair_slot;     // [T * k]
   float* h;               // [rows, F]
   float* xn;              // [T, H]: the batched kernels' pre-split input rows
+  float* o;               // [rows, H]: the batched down's slot outputs
+  int32_t* done;          // [H / 128]: the batched down's counters (zero between launches)
   int32_t* count;         // sanitised-pair count of the permutation
 };
 

@@ -123,13 +123,18 @@ def test_fused_decode_layer_full_size(name, T, n_check):
     assert_close(y.cpu().numpy()[toks], ref, REL_L2_GEMV, f"fused {name} T={T}")
 
 
-# row lengths whose lane geometry is 4 or 8 lanes of 3 blocks (hidden 384 and 768, FFN 384)
+# row lengths whose lane geometry is 4 or 8 lanes of 3 blocks (hidden 384 and 768, FFN 384);
+# hidden 320 (5 blocks of 64 and an odd half of 128) takes the matrix-core path's fallback
+# kernels (a gate/up workgroup of 64 FFN rows, a down workgroup of 16 output rows)
 ODD_SHAPES = {
     "h384_f384": Workload(name="h384_f384", cfg_id=7,
                           shape=LayerShape(hidden=384, ffn=384, n_experts=16, top_k=3, n_shared=1,
                                            gating=SIGMOID, renormalize=1), layers=1),
     "h768_f384": Workload(name="h768_f384", cfg_id=8,
                           shape=LayerShape(hidden=768, ffn=384, n_experts=16, top_k=2, n_shared=1,
+                                           gating=SIGMOID, renormalize=1), layers=1),
+    "h320_f256": Workload(name="h320_f256", cfg_id=12,
+                          shape=LayerShape(hidden=320, ffn=256, n_experts=16, top_k=3, n_shared=1,
                                            gating=SIGMOID, renormalize=1), layers=1),
 }
 
