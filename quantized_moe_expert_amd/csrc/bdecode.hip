@@ -163,64 +163,97 @@ __device__ __forceinline__ void fill_tab_rep(uint32_t* s_tab) {
     s_tab[i] = pair_table_entry(i / kTabRep);
 }
 
-// A cooperative workgroup's stage: the weights of 128 rows x S block pairs (36 S bytes a row),
-// then up to 16 activation rows of 2 S blocks (128 bytes a block: 16 hi pair dwords, then 16
-// lo), each row padded by 16 bytes so that the 16 rows of a fragment read hit distinct banks.
-// Weights arrive as PB-byte pieces, activations as 16-byte pieces, every thread taking
-// pieces tid, tid + 256, ...
-template <int S, int PB>
+// A cooperative workgroup's stage (one step): the weights of 128 rows x S block pairs (36 S
+// bytes a row), then up to 16 activation rows of 2 S blocks (128 bytes a block: 16 hi pair
+// dwords, then 16 lo), each row padded by 16 bytes so that the 16 rows of a fragment read hit
+// distinct banks.
+template <int S>
 struct Stage {
-  static_assert((PB == 16 || PB == 8) && (36 * S) % PB == 0, "whole weight pieces a step");
-  static constexpr int PPR = 36 * S / PB;                  // weight pieces of a row a step
-  static constexpr int NPB = 128 * PPR;                    // weight pieces a step
-  static constexpr int NIB = (NPB + kBdThreads - 1) / kBdThreads;
-  static constexpr int PPA = 16 * S;                       // activation pieces of a row a step
-  static constexpr int NIA = kDecodeMaxTokens * PPA / kBdThreads;
   static constexpr int SB = 128 * 36 * S;                  // weight bytes of a stage
   static constexpr int AROW = 256 * S + 16;                // bytes of an activation row
   static constexpr int STG = SB + kDecodeMaxTokens * AROW; // bytes of a stage
 };
 
-// The K loop of a cooperative workgroup (4 waves): every step's pieces are fetched two steps
-// ahead into registers, written to one of two LDS stages, one barrier a step, and wave w then
-// multiplies stage rows 32 w + 16 t + (0..15) (tile t = 0, 1) by the m activation rows into
-// acc[t] (the matrix instruction's result layout: lane l holds column l % 16, rows
-// 4 (l / 16) .. + 3).  boff / bdst: this thread's weight pieces (byte offset in wrs at step 0;
-// byte offset in the stage, or -1 for none); aoff / adst: its activation pieces (kOob past the
-// m rows: zeros).  A step advances the weight offsets by 36 S bytes and the activation offsets
-// by 256 S.  s_stg: two stages of Stage<S, PB>::STG bytes; s_tab: kTabRep interleaved copies of
-// the pair table (fill_tab_rep).
-template <int S, int PB>
-__device__ __forceinline__ void staged_kloop(
-    __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t xrs,
-    const uint32_t (&boff)[Stage<S, PB>::NIB], const int (&bdst)[Stage<S, PB>::NIB],
-    const uint32_t (&aoff)[Stage<S, PB>::NIA], const int (&adst)[Stage<S, PB>::NIA], int nsteps,
-    int m, int wave, int lane, uint8_t* s_stg, const uint32_t* s_tab, f32x4_t (&acc)[2]) {
-  using G = Stage<S, PB>;
-  typedef uint32_t piece_t __attribute__((ext_vector_type(PB / 4)));
-  piece_t rb[2][G::NIB];
-  u32x4_t ra[2][G::NIA];
-  auto issue = [&](int slot, int st) __attribute__((always_inline)) {
-    st = st < nsteps ? st : nsteps - 1;          // past the end: the last step again, unused
+// The K loop of a cooperative workgroup (4 waves).  Loads go out two steps at a time: each
+// stage row's 72 S bytes of two steps as 16-byte pieces of one contiguous run (a row's bytes
+// then reach memory in runs twice as long as one step's), the activation rows' 512 S bytes
+// likewise; at a double step's start the pieces are written to both LDS stages and the next
+// double step's loads are issued into the same registers, so they have two steps of compute
+// to arrive.  Wave w multiplies stage rows 32 w + 16 t + (0..15) (tile t = 0, 1) by the m
+// activation rows into acc[t] (the matrix instruction's result layout: lane l holds column
+// l % 16, rows 4 (l / 16) .. + 3).  wrow(rr): byte offset in wrs of stage row rr's first
+// block; arow(i): byte offset in xrs of activation row i, kOob past the m rows (zeros).
+// s_stg: two stages of Stage<S>::STG bytes; s_tab: kTabRep interleaved copies of the pair
+// table (fill_tab_rep).
+template <int S, bool KS, typename WRow, typename Route, typename ARow>
+__device__ __forceinline__ bool staged_kloop(__amdgpu_buffer_rsrc_t wrs,
+                                             __amdgpu_buffer_rsrc_t xrs, WRow wrow, Route route,
+                                             ARow arow, int nsteps, int wave, int lane,
+                                             uint8_t* s_stg, const uint32_t* s_tab,
+                                             f32x4_t (&acc)[2]) {
+  using G = Stage<S>;
+  constexpr int RB = 36 * S;                       // weight bytes of a stage row (a step)
+  constexpr int AB = 256 * S;                      // activation bytes of a stage row
+  constexpr int PPW = 2 * RB / 16;                 // 16-byte pieces of a row, two steps
+  constexpr int NPW = 128 * PPW;
+  constexpr int NIW = (NPW + kBdThreads - 1) / kBdThreads;
+  constexpr int PPA = 2 * AB / 16;
+  constexpr int NIA = kDecodeMaxTokens * PPA / kBdThreads;
+  static_assert((2 * RB) % 16 == 0 && NIA * kBdThreads == kDecodeMaxTokens * PPA, "pieces");
+  const int tid = threadIdx.x;
+  // this thread's pieces: weight piece p = tid + 256 i is bytes 16 j .. 16 j + 15 of stage row
+  // rr's two steps (two 8-byte halves, each in the stage of its step); activation piece
+  // p = tid + 256 i is bytes 16 j .. of activation row p / PPA's two steps
+  uint32_t woff[NIW];
+  int wd0[NIW], wd1[NIW];
 #pragma unroll
-    for (int i = 0; i < G::NIB; ++i) {
-      if constexpr (PB == 16)
-        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)boff[i], 36 * S * st, 0);
-      else
-        rb[slot][i] = __builtin_amdgcn_raw_buffer_load_b64(wrs, (int)boff[i], 36 * S * st, 0);
-    }
+  for (int i = 0; i < NIW; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int pp = p < NPW ? p : NPW - 1;
+    const int rr = pp / PPW, j = pp - rr * PPW;
+    woff[i] = wrow(rr) + 16u * j;
+    const int x0 = 16 * j, x1 = 16 * j + 8;
+    wd0[i] = p < NPW ? (x0 < RB ? 0 : G::STG) + rr * RB + (x0 < RB ? x0 : x0 - RB) : -1;
+    wd1[i] = (x1 < RB ? 0 : G::STG) + rr * RB + (x1 < RB ? x1 : x1 - RB);
+  }
+  const int nds = (nsteps + 1) >> 1;               // double steps
+  u32x4_t rw[NIW], ra[NIA];
+  auto issue_w = [&](int d) __attribute__((always_inline)) {
+    d = d < nds ? d : nds - 1;                     // past the end: the last again, unused
 #pragma unroll
-    for (int i = 0; i < G::NIA; ++i)
-      ra[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 256u * S * st),
-                                                          0, 0);
+    for (int i = 0; i < NIW; ++i)
+      rw[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff[i], 2 * RB * d, kNt);
   };
-  auto stage_write = [&](int slot) __attribute__((always_inline)) {
-    uint8_t* sb = s_stg + slot * G::STG;
+  // (issuing the first weights before the routing, for the experts nobody picked as well,
+  // measured slower)
+  const int m = route();
+  if (m <= 0) return false;
+  issue_w(0);
+  uint32_t aoff[NIA];
+  int ad[NIA];
 #pragma unroll
-    for (int i = 0; i < G::NIB; ++i)
-      if (bdst[i] >= 0) *reinterpret_cast<piece_t*>(sb + bdst[i]) = rb[slot][i];
+  for (int i = 0; i < NIA; ++i) {
+    const int p = tid + kBdThreads * i;
+    const int it = p / PPA, j = p - it * PPA;
+    aoff[i] = arow(it, m) + 16u * j;
+    const int x = 16 * j;
+    ad[i] = (x < AB ? 0 : G::STG) + G::SB + it * G::AROW + (x < AB ? x : x - AB);
+  }
+  auto issue_a = [&](int d) __attribute__((always_inline)) {
+    d = d < nds ? d : nds - 1;
 #pragma unroll
-    for (int i = 0; i < G::NIA; ++i) *reinterpret_cast<u32x4_t*>(sb + adst[i]) = ra[slot][i];
+    for (int i = 0; i < NIA; ++i)
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(aoff[i] + 2u * AB * d), 0, 0);
+  };
+  auto stage_write = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) *reinterpret_cast<u32x4_t*>(s_stg + ad[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      if (wd0[i] >= 0) {
+        *reinterpret_cast<u32x2_t*>(s_stg + wd0[i]) = u32x2_t{rw[i][0], rw[i][1]};
+        *reinterpret_cast<u32x2_t*>(s_stg + wd1[i]) = u32x2_t{rw[i][2], rw[i][3]};
+      }
   };
 
   const int c16 = lane & 15, q = lane >> 4;
@@ -232,14 +265,36 @@ __device__ __forceinline__ void staged_kloop(
     ah[i] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
     al[i] = ah[i];
   }
-  const bool arow = c16 < m;
+  const bool live = c16 < m;       // this lane's activation row is one of the m
   const uint32_t* tabl = s_tab + (lane % kTabRep);
+  // KS: the two waves of a pair (2 h, 2 h + 1) split each step's two block pairs (wave parity
+  // kh takes block pair kh) over both of their row groups (stage rows 64 h .. 64 h + 63, four
+  // tiles), so each activation fragment read serves four tiles, not two; an exchange through
+  // LDS after the loop leaves each wave with the sums of its own two tiles.
+  static_assert(!KS || S == 2, "the K split takes one block pair a wave");
+  const int kh = wave & 1, rh = wave >> 1;
+  f32x4_t acc4[4] = {};
   auto compute = [&](int slot) __attribute__((always_inline)) {
     const uint8_t* sb = s_stg + slot * G::STG;
     const uint8_t* sa = sb + G::SB + c16 * G::AROW + 16 * q;
+    if constexpr (KS) {
+      if (live) {
+        ah[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * kh);
+        ah[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * kh + 128);
+        al[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * kh + 64);
+        al[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * kh + 192);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t* rw = reinterpret_cast<const uint32_t*>(
+            sb + (64 * rh + 16 * t + c16) * 36 * S + 36 * kh);
+        tile_pair_lds<kTabRep>(rw, q, ah, al, tabl, acc4[t]);
+      }
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < S; ++b) {
-      if (arow) {
+      if (live) {
         ah[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b);
         ah[1] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 128);
         al[0] = *reinterpret_cast<const bf16x8_t*>(sa + 256 * b + 64);
@@ -254,23 +309,37 @@ __device__ __forceinline__ void staged_kloop(
     }
   };
 
-  issue(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int st = 0; st < nsteps; st += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u == 0 || st + 1 < nsteps) {
-        stage_write(u);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(u, st + u + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        compute(u);
-      }
-    }
+  issue_a(0);
+  for (int d = 0; d < nds; ++d) {
+    lds_barrier();                                 // every wave is done with both stages
+    stage_write();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(d + 1);
+    issue_w(d + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    compute(0);
+    if (2 * d + 1 < nsteps) compute(1);
   }
+  if constexpr (KS) {
+    // wave 2 h + kh keeps tiles 2 kh, 2 kh + 1 of its pair's four: it hands the other two
+    // partial sums to its partner and adds the partner's partials of its own
+    __syncthreads();                               // every wave is done with the stages
+    float* s_x = reinterpret_cast<float*>(s_stg);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_x[((wave * 2 + tt) * 4 + r) * 64 + lane] = kh ? acc4[tt][r] : acc4[2 + tt][r];
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[tt][r] = (kh ? acc4[2 + tt][r] : acc4[tt][r]) +
+                     s_x[(((wave ^ 1) * 2 + tt) * 4 + r) * 64 + lane];
+  }
+  return true;
 }
 
 // The route table of T tokens by one workgroup of 256 threads: top-k and gating weights of
@@ -404,13 +473,13 @@ __global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
-  const int P = T * k;
   const int y = blockIdx.y;
   if (y == E + S) {                       // the route-table workgroup (grid column 0 only)
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0) {
       publish_routes(logits, T, E, S, k, gating, renorm, ids_out, w_out, offsets_out, sp_out,
                      ps_out, s_ids, s_w, s_cnt, s_off, s_wave);
       for (int i = tid; i < (H >> 7); i += kBdThreads) done[i] = 0;   // the down's counters
+    }
     return;
   }
   s_tab[tid] = pair_table_entry(tid);
@@ -499,15 +568,14 @@ __global__ void __launch_bounds__(kBdThreads) bdec_gateup_kernel(
 
 
 // Workgroup-cooperative variant: the 4 waves take 64 FFN rows (a gate and an up tile each) and
-// walk K in steps of S block pairs together.  Each step's weights (128 rows x 36 S bytes) and
-// activations (up to 16 token rows x 2 S blocks x 128 bytes) are fetched as whole PB-byte
-// pieces of contiguous memory by all 256 threads, two steps ahead into registers, then written
-// to one of two LDS stages; one barrier a step; the waves read their operands from LDS.  Every
-// cache line of the weights is then read by one instruction, where the direct variant above
-// reads 20 bytes of each of 16 rows an instruction.  Needs rows of a multiple of PB bytes and
-// whole steps (H / 64 a multiple of S).  At most three waves a SIMD: the schedule the compiler
-// makes in that register budget measured faster than with four (or two).
-template <int S, int PB>
+// walk K together (staged_kloop): the weights of 128 rows and the activations are fetched as
+// whole 16-byte pieces of contiguous memory by all 256 threads, two steps at a time, into LDS;
+// the waves read their operands from LDS.  Every cache line of the weights is then read by
+// one instruction, where the direct variant above reads 20 bytes of each of 16 rows an
+// instruction.  Needs whole steps (H / 64 a multiple of S).  At most three waves a SIMD: the
+// schedule the compiler makes in that register budget measured faster than with four (or
+// two).
+template <int S>
 __global__ void __launch_bounds__(kBdThreads) __attribute__((amdgpu_waves_per_eu(1, 3)))
 bdec_gateup2_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ xhl,
@@ -515,9 +583,7 @@ bdec_gateup2_kernel(
     int renorm, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int32_t* __restrict__ offsets_out, int32_t* __restrict__ sp_out,
     int32_t* __restrict__ ps_out, uint32_t* __restrict__ hhl, int32_t* __restrict__ done) {
-  using G = Stage<S, PB>;
-  constexpr int PPR = G::PPR, NPB = G::NPB, NIB = G::NIB, PPA = G::PPA, NIA = G::NIA;
-  constexpr int SB = G::SB, AROW = G::AROW, STG = G::STG;
+  constexpr int STG = Stage<S>::STG;
   static_assert(2 * STG >= (int)(2 * kDecodeMaxTokens * kBdMaxK * 4 + 2 * (kMaxE + 1) * 4 + 16),
                 "the route-table workgroup's arrays share the stage memory");
   // the pair table first (LDS address 0: a lookup address is the code byte times 4), then the
@@ -547,9 +613,6 @@ bdec_gateup2_kernel(
     return;
   }
   fill_tab_rep(s_tab);
-  route_expert(logits, T, E, k, y, s_rank, s_tok, s_prow, &s_m);
-  const int m = s_m;
-  if (m == 0) return;
   const int ex = y < E ? y : E;
   const int NBH = H >> 5, NBF = F >> 5;
   const int nsteps = (NBH >> 1) / S;
@@ -557,36 +620,26 @@ bdec_gateup2_kernel(
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(bank + (int64_t)ex * stride, 2u * F * rowb);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xhl, (uint32_t)T * (uint32_t)H * 4u);
 
-  // the pieces this thread copies: weight piece p = tid + 256 i is 16-byte piece j of stage
-  // row rr = p / PPR; stage row rr = 32 w + 16 t + c is column c of wave w's gate (t = 0) or
-  // up (t = 1) tile; wave w takes FFN block 2 blockIdx.x + w / 2, half w % 2, and column c is
-  // FFN row 32 block + 8 half + (c % 8) + 16 (c / 8) (a row and the row 16 above it, one
-  // code-byte pair of h, in lanes c and c + 8)
-  uint32_t boff[NIB];
-  int bdst[NIB];
-#pragma unroll
-  for (int i = 0; i < NIB; ++i) {
-    const int p = tid + kBdThreads * i;
-    const int pp = p < NPB ? p : NPB - 1;
-    const int rr = pp / PPR, j = pp - rr * PPR;
+  // stage row rr = 32 w + 16 t + c is column c of wave w's gate (t = 0) or up (t = 1) tile;
+  // wave w takes FFN block 2 blockIdx.x + w / 2, half w % 2, and column c is FFN row
+  // 32 block + 8 half + (c % 8) + 16 (c / 8) (a row and the row 16 above it, one code-byte
+  // pair of h, in lanes c and c + 8)
+  auto wrow = [&](int rr) __attribute__((always_inline)) {
     const int w = rr >> 5, t = (rr >> 4) & 1, c = rr & 15;
     const uint32_t f = 32 * (2 * blockIdx.x + (w >> 1)) + 8 * (w & 1) + (c & 7) + 16 * (c >> 3);
-    boff[i] = (t ? F + f : f) * rowb + (uint32_t)PB * j;
-    bdst[i] = p < NPB ? PB * p : -1;
-  }
-  // activation piece p = tid + 256 i: piece j of token row i_t = p / PPA (zeros past m)
-  uint32_t aoff[NIA];
-  int adst[NIA];
-#pragma unroll
-  for (int i = 0; i < NIA; ++i) {
-    const int p = tid + kBdThreads * i;
-    const int it = p / PPA, j = p - it * PPA;
-    aoff[i] = it < m ? (uint32_t)s_tok[it] * (uint32_t)NBH * 128u + 16u * j : kOob;
-    adst[i] = SB + it * AROW + 16 * j;
-  }
+    return (t ? F + f : f) * rowb;
+  };
+  auto route = [&]() __attribute__((always_inline)) {
+    route_expert(logits, T, E, k, y, s_rank, s_tok, s_prow, &s_m);
+    return s_m;
+  };
+  auto arow = [&](int it, int m) __attribute__((always_inline)) {
+    return it < m ? (uint32_t)s_tok[it] * (uint32_t)NBH * 128u : kOob;
+  };
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  staged_kloop<S, PB>(wrs, xrs, boff, bdst, aoff, adst, nsteps, m, wave, lane, s_stg, s_tab,
-                      acc);
+  if (!staged_kloop<S, true>(wrs, xrs, wrow, route, arow, nsteps, wave, lane, s_stg, s_tab, acc))
+    return;                                        // no token picked the expert
+  const int m = s_m;
   const int c16 = lane & 15, q = lane >> 4;
 
   // h = silu(g) * u; lane c16 < 8 takes the row 16 above from lane c16 + 8 and writes the
@@ -911,13 +964,13 @@ __global__ void __launch_bounds__(kBdDownWaves * 64) bdec_down2_kernel(
 // fixed order (routed j = 0..k-1, the shared expert, the residual) and clears the counter.
 // Every expert's h is then read once a row range, where the per-16-row kernel above reads it
 // once every 16 rows.  Needs H a multiple of 128 and whole steps (F / 64 a multiple of S).
-template <int S, int PB>
+template <int S>
 __global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
     const uint8_t* __restrict__ bank, int64_t stride, const uint32_t* __restrict__ hhl,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
     const float* __restrict__ w, int T, int H, int F, int E, int NS, int k, float* o,
     int32_t* __restrict__ done, const float* residual, float* y) {
-  using G = Stage<S, PB>;
+  using G = Stage<S>;
   __shared__ __align__(16) uint8_t s_mem[1024 * kTabRep + 2 * G::STG];
   uint32_t* s_tab = reinterpret_cast<uint32_t*>(s_mem);
   uint8_t* s_stg = s_mem + 1024 * kTabRep;
@@ -942,30 +995,13 @@ __global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
       make_rsrc(bank + (int64_t)ex * stride + down_off + (int64_t)r0 * rowb, 128u * rowb);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(hhl, (uint32_t)nslots * (uint32_t)F * 4u);
 
-  // weight piece p = tid + 256 i: piece j of stage row (output row r0 +) rr = p / PPR
-  uint32_t boff[G::NIB];
-  int bdst[G::NIB];
-#pragma unroll
-  for (int i = 0; i < G::NIB; ++i) {
-    const int p = tid + kBdThreads * i;
-    const int pp = p < G::NPB ? p : G::NPB - 1;
-    const int rr = pp / G::PPR, j = pp - rr * G::PPR;
-    boff[i] = (uint32_t)rr * rowb + (uint32_t)PB * j;
-    bdst[i] = p < G::NPB ? PB * p : -1;
-  }
-  // activation piece p = tid + 256 i: piece j of the h row of slot i_t = p / PPA (zeros past m)
-  uint32_t aoff[G::NIA];
-  int adst[G::NIA];
-#pragma unroll
-  for (int i = 0; i < G::NIA; ++i) {
-    const int p = tid + kBdThreads * i;
-    const int it = p / G::PPA, j = p - it * G::PPA;
-    aoff[i] = it < m ? (uint32_t)s_prow[it] * (uint32_t)NBF * 128u + 16u * j : kOob;
-    adst[i] = G::SB + it * G::AROW + 16 * j;
-  }
+  auto wrow = [&](int rr) __attribute__((always_inline)) { return (uint32_t)rr * rowb; };
+  auto route = [&]() __attribute__((always_inline)) { return m; };
+  auto arow = [&](int it, int mm) __attribute__((always_inline)) {
+    return it < mm ? (uint32_t)s_prow[it] * (uint32_t)NBF * 128u : kOob;
+  };
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-  staged_kloop<S, PB>(wrs, xrs, boff, bdst, aoff, adst, nsteps, m, wave, lane, s_stg, s_tab,
-                      acc);
+  staged_kloop<S, false>(wrs, xrs, wrow, route, arow, nsteps, wave, lane, s_stg, s_tab, acc);
   // o is stored at the device-coherent level (sc1: as the compiler's device-scope atomic
   // stores), so no workgroup has to write back its L2 (a device-scope release fence writes back
   // the XCD's whole L2: one a workgroup made this kernel four times slower).  Each thread waits
@@ -1065,7 +1101,7 @@ hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t st
     // workgroups a routed expert's worth of rows
     if ((sh.H / 64) % 2 == 0) {
       const dim3 grid(sh.F / 64, sh.E + sh.S + 1);
-      hipLaunchKernelGGL((bdec_gateup2_kernel<2, 8>), grid, dim3(kBdThreads), 0, s, bank, stride,
+      hipLaunchKernelGGL((bdec_gateup2_kernel<2>), grid, dim3(kBdThreads), 0, s, bank, stride,
                          xhl, sc.logits, T, sh.H, sh.F, sh.E, sh.S, sh.k, sh.gating, sh.renorm,
                          sc.ids, sc.w, sc.offsets, sc.sorted_pairs, sc.pair_slot, hhl,
                          sc.done);
@@ -1082,7 +1118,7 @@ hipError_t launch_bdecode_layer(const Shape& sh, const uint8_t* bank, int64_t st
   }
   if (stages & 4) {
     if (sh.H % 128 == 0 && (sh.F / 64) % 2 == 0)
-      hipLaunchKernelGGL((bdec_down3_kernel<2, 8>), dim3(sh.H / 128, sh.E + sh.S),
+      hipLaunchKernelGGL((bdec_down3_kernel<2>), dim3(sh.H / 128, sh.E + sh.S),
                          dim3(kBdThreads), 0, s, bank, stride, hhl, sc.offsets, sc.sorted_pairs,
                          sc.w, T, sh.H, sh.F, sh.E, sh.S, sh.k, sc.o, sc.done, residual, y);
     else if ((sh.F / 64) % 2 == 0)
