@@ -425,10 +425,10 @@ def batched_traffic(wl, d):
     if d["T"] <= 4:
         return {}
     gu_grid = (s.ffn // 64) * (s.n_experts + s.n_shared + 1) * 256
-    dn_grid = (s.hidden // 16) * 512
-    return {"gate_up_traffic_bytes": traffic("bdec_gateup2_kernel<2, 8>", gu_grid),
+    dn_grid = (s.hidden // 128) * (s.n_experts + s.n_shared) * 256
+    return {"gate_up_traffic_bytes": traffic("bdec_gateup2_kernel<2>", gu_grid),
             "gate_up_algorithmic_bytes": round(d["gate_up_bytes"]),
-            "down_traffic_bytes": traffic("bdec_down2_kernel<2>", dn_grid),
+            "down_traffic_bytes": traffic("bdec_down3_kernel<2>", dn_grid),
             "down_algorithmic_bytes": round(d["down_bytes"])}
 
 

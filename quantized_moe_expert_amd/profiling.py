@@ -28,6 +28,7 @@ KERNEL_SOURCES = {
     "gemm_kernel<false>": ("gemm.hip", "common.h", "kernels.h"),
     "bdec_gateup2_kernel": ("bdecode.hip", "common.h", "route_core.h", "kernels.h"),
     "bdec_down2_kernel": ("bdecode.hip", "common.h", "route_core.h", "kernels.h"),
+    "bdec_down3_kernel": ("bdecode.hip", "common.h", "route_core.h", "kernels.h"),
 }
 PMC_FILE = "pmc_traffic_decode_and_prefill_all_workloads.txt"
 
