@@ -103,6 +103,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// silu from the hardware base-2 exponential and reciprocal (a few ulp of fp32): for results
+// rounded to bf16 right after, where the library exp and the IEEE division cost five times
+// the instructions.  e^-g = 2^(-g log2 e); overflow gives 1/inf = 0, so g -> -inf gives -0.
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64); every lane of
 // the group ends with the group sum.  Fixed butterfly order: deterministic.
 __device__ __forceinline__ float group_sum(float v, int width) {

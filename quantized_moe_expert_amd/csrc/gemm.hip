@@ -342,33 +342,41 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
   wait_vm<0>();                           // no copy may land in LDS after the tile is done
 
   // epilogue: lane (c32, h) holds column c32 of each 32 x 32 tile; register e is row
-  // 8 (e / 4) + 4 h + e % 4
+  // 8 (e / 4) + 4 h + e % 4.  Stores go through a buffer resource over the tile's valid rows
+  // (rows past rows_valid fall past its end and are dropped, as are stores at offset kOff):
+  // one 32-bit offset a store, no 64-bit address arithmetic
+  constexpr uint32_t kOff = 0x80000000u;
   if (GATEUP) {
-    uint16_t* hout = static_cast<uint16_t*>(out);
     const int col = nt * 128 + 16 * wave + (c32 & 15);
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint16_t*>(out) + row0 * (int64_t)F, 0, rows_valid * F * 2, 0x00020000);
+    // lanes c32 >= 16 hold the up values: they store nothing
+    const uint32_t vbase = c32 < 16 ? (uint32_t)(4 * h * F + col) * 2u : kOff;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float g = acc[r][e];
         const float u = __shfl_xor(g, 16, 64);         // the up value of the same output
-        const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (c32 >= 16 || m >= rows_valid) continue;
-        const float hv = silu(g) * u;
-        hout[(row0 + m) * (int64_t)F + col] = (uint16_t)(pack_bf16x2(hv, 0.0f) & 0xFFFFu);
+        const float hv = silu_fast(g) * u;             // h is rounded to bf16 at once
+        const uint32_t mo = (uint32_t)(32 * r + 8 * (e >> 2) + (e & 3)) * (uint32_t)F * 2u;
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(hv, 0.0f) & 0xFFFFu), hrs,
+                                              (int)(vbase + mo), 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);          // one row group's values live at a time
     }
   } else {
-    float* oout = static_cast<float*>(out);
     const int col = nt * kBN + 32 * wave + c32;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<float*>(out) + row0 * (int64_t)H, 0, rows_valid * H * 4, 0x00020000);
+    const uint32_t vbase = col < H ? (uint32_t)(4 * h * H + col) * 4u : kOff;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = 32 * r + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m >= rows_valid || col >= H) continue;
-        oout[(row0 + m) * (int64_t)H + col] = acc[r][e];
+        const uint32_t mo = (uint32_t)(32 * r + 8 * (e >> 2) + (e & 3)) * (uint32_t)H * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r][e]), ors, (int)(vbase + mo),
+                                              0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
