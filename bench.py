@@ -84,7 +84,7 @@ def gemm_grid(shape, tokens, stage):
     rows = tokens * (shape.top_k + shape.n_shared)
     mtiles = -(-rows // 256) + min(shape.n_experts + shape.n_shared, rows)
     nt = shape.ffn // 128 if stage == 0 else -(-shape.hidden // 256)
-    return -(-mtiles * nt // 8) * 8 * 512
+    return -(-mtiles // 8) * 8 * nt * 512
 
 
 # ---- CPU baseline (the oracle), run before the GPU is touched ----------------------------
