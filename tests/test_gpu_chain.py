@@ -98,10 +98,12 @@ def test_chain_38_layers_vs_per_layer_path():
     assert torch.equal(x2, x)
 
 
-def test_chain_graph_replay():
+@pytest.mark.parametrize("T", [1, 16])
+def test_chain_graph_replay(T):
+    # T = 16: the batched kernels, whose down stage counts finished workgroups in the
+    # workspace (cleared by the gate/up launch and by the workgroup that combines)
     wl = XING4_DECODE
     s = wl.shape
-    T = 1
     layers, keep = _layers(wl, 6)
     arr = M.make_layers([(bank, wr, bias) for (wr, bias, bank) in layers])
     x0 = L.make_activations(wl, T)
