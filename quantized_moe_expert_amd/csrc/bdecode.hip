@@ -182,9 +182,10 @@ struct Stage {
 // to arrive.  Wave w multiplies stage rows 32 w + 16 t + (0..15) (tile t = 0, 1) by the m
 // activation rows into acc[t] (the matrix instruction's result layout: lane l holds column
 // l % 16, rows 4 (l / 16) .. + 3).  wrow(rr): byte offset in wrs of stage row rr's first
-// block; arow(i): byte offset in xrs of activation row i, kOob past the m rows (zeros).
-// s_stg: two stages of Stage<S>::STG bytes; s_tab: kTabRep interleaved copies of the pair
-// table (fill_tab_rep).
+// block; route(): the caller's routing, run once the weight pieces are set up, returning m,
+// the activation rows (none: the loop returns false at once); arow(i, m): byte offset in xrs
+// of activation row i, kOob past the m rows (zeros).  KS: see below.  s_stg: two stages of
+// Stage<S>::STG bytes; s_tab: kTabRep interleaved copies of the pair table (fill_tab_rep).
 template <int S, bool KS, typename WRow, typename Route, typename ARow>
 __device__ __forceinline__ bool staged_kloop(__amdgpu_buffer_rsrc_t wrs,
                                              __amdgpu_buffer_rsrc_t xrs, WRow wrow, Route route,
