@@ -1030,7 +1030,7 @@ __global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // drop stale cached lines of o
   // thread (c, u0) = (tid % 128, tid / 128) combines column r0 + c of tokens u0, u0 + 2, ..;
-  // the loads of two routed terms of every token go out together (a few round trips in all)
+  // the loads of four routed terms of every token go out together (one round trip at k = 4)
   constexpr int NU = kDecodeMaxTokens / 2;
   const int r = r0 + (tid & 127), u0 = tid >> 7;
   const __amdgpu_buffer_rsrc_t wrr = make_rsrc(w, (uint32_t)P * 4u);
@@ -1044,10 +1044,10 @@ __global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
                 ors, ok && NS > 0 ? (int)(((uint32_t)(P + t) * H + r) * 4u) : (int)kOob, 0, kSc1));
     rs[u] = ok && residual ? residual[(int64_t)t * H + r] : 0.0f;
   }
-  for (int j0 = 0; j0 < k; j0 += 2) {
-    float v[2][NU], wv[2][NU];
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    float v[4][NU], wv[4][NU];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int t = u0 + 2 * u, j = j0 + jj;
@@ -1059,7 +1059,7 @@ __global__ void __launch_bounds__(kBdThreads) bdec_down3_kernel(
                         wrr, ok ? (t * k + j) * 4 : (int)kOob, 0, 0));
       }
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int u = 0; u < NU; ++u)
         if (j0 + jj < k) a[u] = fmaf(wv[jj][u], v[jj][u], a[u]);
