@@ -13,14 +13,16 @@
 //
 //   activations  copied from HBM straight into LDS by the LDS-direct loads of gfx950
 //                (global_load_lds_dwordx4: no registers, no LDS write instructions), one
-//                instruction per 8 whole rows (coalesced), into a ring of 4 stages filled
-//                two and three steps ahead (K steps go in pairs, one wait and one barrier a
-//                pair), the copies of a step spread evenly over the eight waves; the 16-byte
+//                instruction per 8 whole rows (coalesced), into a ring of 2 G stages (K
+//                steps go in groups of G, one wait and one barrier a group; G = 2, or 4 for
+//                tiles of at most 64 rows), the copies of a step spread evenly over the eight
+//                waves; the 16-byte
 //                chunks of a row are XOR-swizzled so that every fragment read is a
 //                conflict-free ds_read_b128, and the reads run five matrix instructions
 //                ahead of their use;
-//   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, 4 steps
-//                ahead (a ring of 4 register slots), and dequantises them there; each weight
+//   weights      never touch LDS: each lane loads whole 18-byte blocks into registers, a
+//                group ahead (a ring of 2 G register slots, through a buffer resource with
+//                the step's offset in a scalar register), and dequantises them there; each weight
 //                row belongs to one wave, so every weight is dequantised once a workgroup and
 //                is shared by its 256 slot rows.
 //
@@ -56,8 +58,6 @@ namespace moe {
 constexpr int kBM = 256;                 // slot rows per tile
 constexpr int kBN = 256;                 // weight rows per tile
 constexpr int kKS = 64;                  // k per step (2 IQ4_NL blocks)
-constexpr int kStages = 4;               // activation stages in LDS (filled 2-3 steps ahead)
-constexpr int kBSlots = 4;               // weight-block register slots (filled 4 steps ahead)
 constexpr int kGemmThreads = 512;
 constexpr int kStageBytes = kBM * kKS * 2;     // bf16 activations of one step: 32 KB
 constexpr int kXcds = 8;                  // XCDs of an MI355X (each with its own L2)
@@ -72,7 +72,6 @@ static_assert(kCodebookValues[0] == -kCodebookValues[15] && kCodebookValues[1] =
                   kCodebookValues[4] == -kCodebookValues[11] && kCodebookValues[5] == -kCodebookValues[10] &&
                   kCodebookValues[6] == -kCodebookValues[9] && kCodebookValues[7] == -kCodebookValues[8],
               "the byte-table dequantisation needs a symmetric codebook");
-static_assert(kStages == kBSlots, "one unrolled loop body per stage and slot");
 
 // Byte tables of one block: entry m (0..7) = bf16(d * c[7 - m]), high bytes in h, low in l.
 struct BlockTab {
@@ -153,17 +152,6 @@ __device__ __forceinline__ void wait_lgkm() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
 }
 
-// One 18-byte block as five aligned dwords (two load instructions: 16 + 4 bytes).  Blocks
-// with an even index start 4-byte aligned, odd ones 2 bytes past a dword boundary.
-__device__ __forceinline__ RawBlock load_block2(const uint8_t* row, int blk) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + blk * kBlockBytes - (blk & 1) * 2);
-  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
-  RawBlock r;
-  r.w[0] = a[0]; r.w[1] = a[1]; r.w[2] = a[2]; r.w[3] = a[3];
-  r.w[4] = p[4];
-  return r;
-}
-
 // One workgroup tile: RG 32-row groups of slot rows hold rows of the tile (the rest of the
 // 256 are past the expert's last slot and are neither multiplied nor stored).
 template <bool GATEUP, int RG>
@@ -186,7 +174,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
     wr = nt * kBN + 32 * wave + c32;
     if (wr >= H) wr = H - 1;
   }
-  const uint8_t* brow = wmat + (int64_t)wr * row_bytes;
+  // this lane's blocks 2 kd + h through a buffer resource over the expert's matrix: block
+  // 2 kd + h starts at byte 36 kd + 18 h of the row, read from the dword at 36 kd + 16 h (an
+  // odd block starts 2 bytes past a dword boundary), so a step's offset is the uniform 36 kd
+  // on a per-lane base (no per-step address multiply)
+  const int wrows = GATEUP ? 2 * F : H;
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wmat), 0, (int)(wrows * row_bytes), 0x00020000);
+  const uint32_t bvoff = (uint32_t)(wr * row_bytes) + 16u * h;
 
   // Activations of a step in LDS: row-major, 256 rows x 8 chunks of 16 bytes (8 k each);
   // chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that read rows
@@ -198,7 +193,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
   // group, the same bytes to the same place.  Every wave issues the same number of copies
   // (NA), so the vector-memory counts of all waves agree and no branch surrounds a load (a
   // branch around loads makes the compiler drain every outstanding load where the paths
-  // meet).  n < 4 RG: inside the 32 KB stage.  Rows past rows_valid repeat row 0.
+  // meet).  n < 4 RG: inside the stage (RG x 4 KB).  Rows past rows_valid repeat row 0.
   constexpr int NA = (RG + 1) / 2;
   const uint16_t* tile_in = in + row0 * (int64_t)K;              // uniform
   uint32_t arow[NA];                        // element offsets from tile_in (< 256 K)
@@ -214,70 +209,71 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff[i] = c32 * 128 + (((4 * h + i) ^ ((c32 >> 1) & 7)) << 4);
 
-  // The four stages are four LDS arrays, not one: the compiler then knows that reads of one
-  // stage do not alias copies into another and adds no wait of its own between them.
-  auto stage_of = [&](int st) __attribute__((always_inline)) {
-    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
+  // K runs in groups of G steps with one wait and one barrier a group.  A tile of RG row
+  // groups fills RG x 4 KB of a step's stage, so shorter tiles afford deeper rings in the same
+  // 128 KB of LDS: G = 4 for one or two row groups, 2 otherwise (8-step groups for one or two
+  // row groups, and 4-step groups for three or four, measured slower on the skewed loads: a
+  // longer first fill and more clamped loads past the end of a short K).  The stages of a group
+  // come from one half of the LDS (arrays 0 and 1 for even groups, 2 and 3 for odd ones), G
+  // stages of 64 KB / G each; the four arrays are separate, so the compiler knows that the
+  // fragment reads of one group do not alias the copies into the next and adds no wait of
+  // its own between them.
+  constexpr int G = RG > 2 ? 2 : 4;
+  constexpr int SB = 2 * kStageBytes / G;            // bytes of a stage
+  static_assert(RG * 4096 <= SB, "a stage holds the tile's rows of one step");
+  auto stage_of = [&](auto pc, auto jc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value, OFF = decltype(jc)::value * SB;
+    if constexpr (OFF < kStageBytes) return (P ? lds2 : lds0) + OFF;
+    else return (P ? lds3 : lds1) + (OFF - kStageBytes);
   };
-  // copies of step kd into stage st (kd clamped to the last step: the same instruction count
-  // every step, which the vmcnt waits below rely on)
-  auto dma_a = [&](int kd, int st) __attribute__((always_inline)) {
+  // copies of step kd into a stage (kd clamped to the last step: the same instructions
+  // every group)
+  auto dma_a = [&](int kd, uint8_t* stage) __attribute__((always_inline)) {
     kd = kd < NKT ? kd : NKT - 1;
-    uint8_t* stage = stage_of(st);
 #pragma unroll
     for (int s = 0; s < NA; ++s)          // rows 8 n .. 8 n + 7
       __builtin_amdgcn_global_load_lds(tile_in + arow[s] + kd * kKS, stage + an[s] * 1024, 16,
                                        0, 0);
   };
-  RawBlock bq[kBSlots];
+  // weight blocks: 2 G register slots, step kt + j of a group of parity P in slot P G + j
+  RawBlock bq[2 * G];
   auto load_b = [&](int kd, RawBlock& dst) __attribute__((always_inline)) {
     kd = kd < NKT ? kd : NKT - 1;
-    dst = load_block2(brow, 2 * kd + h);
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(brs, (int)bvoff, 36 * kd, 0);
+    dst.w[0] = a[0]; dst.w[1] = a[1]; dst.w[2] = a[2]; dst.w[3] = a[3];
+    dst.w[4] = __builtin_amdgcn_raw_buffer_load_b32(brs, (int)(bvoff + 16u), 36 * kd, 0);
   };
 
   f32x16_t acc[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = f32x16_t{};
 
-  // Steps go in pairs (kt, kt + 1), kt even (K is a multiple of 128, so the step count is
-  // even): one wait and one barrier a pair, then the copies of the next pair's two stages,
-  // then the two steps; each step refills its weight slot.  Issue order, pinned by
-  // scheduling barriers (the vmcnt count depends on it): B(0) B(1) A(0) A(1) B(2) B(3), then a
-  // pair kt issues A(kt+2) A(kt+3) B(kt+4) B(kt+5).
-  load_b(0, bq[0]);
-  load_b(1, bq[1]);
-  __builtin_amdgcn_sched_barrier(0);
-  dma_a(0, 0);
-  dma_a(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_b(2, bq[2]);
-  load_b(3, bq[3]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Pair kt (U = kt % 4, 0 or 2): wait until every load of this wave has completed (A(kt)
-  // and A(kt+1) among them), then a barrier: every wave's copies of both stages are in, and
-  // every wave has used its reads of stages (kt+2) % 4 and (kt+3) % 4 from the previous pair.
-  // The wait is a full one (vmcnt(0)): the LDS-direct copies need not complete in issue
-  // order, and a wait for all but the last N loads did not order them -- a producer/consumer
-  // version whose waits let later copies stay in flight read stale activations.  Here the
-  // loads still in flight at a pair's wait are the previous pair's last weight blocks, so the
-  // full wait costs about 4%.  The barrier carries no
-  // memory fence: a workgroup release fence makes the compiler wait for every copy still in
-  // flight (vmcnt(0)), which would undo the prefetch; the explicit waits order the copies,
-  // the lgkmcnt(0) this wave's LDS reads, and the memory clobber keeps the compiler from
-  // moving LDS accesses across.  The scheduling barrier after it keeps the first uses of the
-  // weight slots below the wait, where the compiler has nothing left to wait for.  Every pair
-  // issues the same instructions (step indices past the end are clamped), which the vmcnt
-  // count relies on.
-  constexpr int kOutstanding = 0;
-  auto step = [&](int kt, auto uc) __attribute__((always_inline)) {
-    constexpr int U = decltype(uc)::value;
-    const BlockTab tab = block_tab(bq[U], h != 0);
+  // A group starts with a wait until every load of this wave has completed, then a barrier:
+  // every wave's copies of the group's stages are in, and every wave is done reading the
+  // previous group's stages, which the copies of the next group then overwrite.  The wait is
+  // a full one (vmcnt(0)): the LDS-direct copies need not complete in issue order, and a wait
+  // for all but the last N loads did not order them -- a producer/consumer version whose
+  // waits let later copies stay in flight read stale activations.  So a load has from its
+  // issue to the start of the next group to arrive.  For G = 2 each step refills its weight
+  // slot with the block 4 steps ahead as it takes it (the loads in flight at a wait were
+  // issued during the group, the last one step before it); for G = 4 the whole next group's
+  // weight blocks go out right after the barrier with its copies, so every load has a full
+  // group of steps to arrive: a tile of one or two row groups runs ~850 cycles of
+  // dequantisation a step on each SIMD and a quarter or half of that on the matrix cores,
+  // which a wait one step after the last load left exposed to memory latency (3584/1024 gate/
+  // up over 65 bins of 32 rows: 168 -> 132 us; 7168/384 at 8,192 tokens: gate/up 3,760 ->
+  // 3,543 us, down 2,130 -> 2,014 us).  The
+  // barrier carries no memory fence: a workgroup release fence makes the compiler wait for
+  // every copy still in flight (vmcnt(0)), which would undo the prefetch; the explicit waits
+  // order the copies, the lgkmcnt(0) this wave's LDS reads, and the memory clobber keeps the
+  // compiler from moving LDS accesses across.
+  constexpr bool kEarly = G > 2;
+  auto step = [&](int kt, const uint8_t* stage, RawBlock& blk) __attribute__((always_inline)) {
+    const BlockTab tab = block_tab(blk, h != 0);
     uint32_t code[4];
-    block_codes(bq[U], h != 0, code);
-    load_b(kt + 4, bq[U]);
+    block_codes(blk, h != 0, code);
+    if constexpr (!kEarly) load_b(kt + 2 * G, blk);
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* stage = stage_of(U);
     // Matrix instruction j of the step (j < 4 RG): group I = j / RG (k 16 I .. 16 I + 15),
     // row group r = j % RG.  Its A fragment is read kWin - 1 instructions ahead, so that
     // kWin - 1 LDS reads are in flight behind every matrix instruction instead of one read
@@ -320,25 +316,62 @@ __device__ __forceinline__ void gemm_tile(uint8_t* lds0, uint8_t* lds1, uint8_t*
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto pair = [&](int kt, auto uc) __attribute__((always_inline)) {
-    constexpr int U = decltype(uc)::value;
-    wait_vm<kOutstanding>();
+  // group of steps kt .. kt + G - 1 (kt a multiple of G, parity P = (kt / G) % 2); a tail
+  // group (TAIL) computes only its first nv steps -- its loads and copies still go out, clamped
+  auto group = [&](int kt, auto pc, auto tc, int nv) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    constexpr bool TAIL = decltype(tc)::value;
+    wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    dma_a(kt + 2, (U + 2) % kStages);
-    dma_a(kt + 3, (U + 3) % kStages);
+    static_for<G>([&](auto jc) __attribute__((always_inline)) {
+      dma_a(kt + G + decltype(jc)::value, stage_of(std::integral_constant<int, 1 - P>{}, jc));
+    });
+    if constexpr (kEarly)
+      static_for<G>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        load_b(kt + G + J, bq[(1 - P) * G + J]);
+      });
     __builtin_amdgcn_sched_barrier(0);
-    step(kt, std::integral_constant<int, U>{});
-    step(kt + 1, std::integral_constant<int, U + 1>{});
+    static_for<G>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      if (!TAIL || J < nv) step(kt + J, stage_of(pc, jc), bq[P * G + J]);
+    });
   };
-  // whole groups of two pairs in the loop, the remainder (one pair) after it: no conditional
-  // step inside the loop, whose paths would meet with different outstanding loads
+  // prologue: the first group's weight blocks and copies (and for G = 2 the second group's
+  // weight blocks)
+  static_for<G>([&](auto jc) __attribute__((always_inline)) {
+    load_b(decltype(jc)::value, bq[decltype(jc)::value]);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<G>([&](auto jc) __attribute__((always_inline)) {
+    dma_a(decltype(jc)::value, stage_of(std::integral_constant<int, 0>{}, jc));
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!kEarly)
+    static_for<G>([&](auto jc) __attribute__((always_inline)) {
+      load_b(G + decltype(jc)::value, bq[G + decltype(jc)::value]);
+    });
+  __builtin_amdgcn_sched_barrier(0);
+
+  // whole groups in pairs in the loop (no conditional step inside, whose paths would meet
+  // with different loads outstanding), then the rest: for G = 2 one whole group (K is a
+  // multiple of 128, so the step count is even), for G = 4 up to two tail groups
+  constexpr std::integral_constant<int, 0> kP0{};
+  constexpr std::integral_constant<int, 1> kP1{};
+  constexpr std::false_type kWhole{};
   int kt = 0;
-  for (; kt + kStages <= NKT; kt += kStages) {
-    pair(kt, std::integral_constant<int, 0>{});
-    pair(kt + 2, std::integral_constant<int, 2>{});
+  for (; kt + 2 * G <= NKT; kt += 2 * G) {
+    group(kt, kP0, kWhole, G);
+    group(kt + G, kP1, kWhole, G);
   }
-  if (kt < NKT) pair(kt, std::integral_constant<int, 0>{});
+  const int rest = NKT - kt;
+  if constexpr (kEarly) {
+    if (rest > 0) group(kt, kP0, std::true_type{}, rest);
+    if (rest > G) group(kt + G, kP1, std::true_type{}, rest - G);
+  } else {
+    if (rest > 0) group(kt, kP0, kWhole, G);
+  }
   wait_vm<0>();                           // no copy may land in LDS after the tile is done
 
   // epilogue: lane (c32, h) holds column c32 of each 32 x 32 tile; register e is row

@@ -13,7 +13,8 @@ import quantized_moe_expert_amd as M
 from quantized_moe_expert_amd import layer as L
 from oracle import iq4nl, moe as omoe
 from synth import device as SD, generator as G
-from synth.configs import WORKLOADS, TINY, XING4_DECODE, XING4_PREFILL, QWEN3NEXT_LIKE, DSV41_LIKE
+from synth.configs import (WORKLOADS, TINY, XING4_DECODE, XING4_PREFILL, QWEN3NEXT_LIKE, DSV41_LIKE,
+                           LayerShape, SOFTMAX, Workload)
 
 from .helpers import (REL_L2_GEMV, REL_L2_MFMA, assert_close, assert_within_bound, desc_of,
                       down_bf16_bound, gate_up_bf16_bound, logit_error_bound, oracle_bank,
@@ -345,11 +346,20 @@ def test_grouped_gemm_tile_edges(stage):
             assert_close(got[a:b][:, sample], ref, REL_L2_MFMA, f"edges e={e} {stage}")
 
 
+# K lengths that leave the GEMM's step groups ragged: hidden 384 is 6 steps of 64 (one group of
+# 4 and a tail of 2 for the short tiles' four-step groups), ffn 640 is 10 (a whole pair of
+# groups and a tail of 2)
+_ODD_K = {"h384_f640": Workload(name="h384_f640", cfg_id=13,
+                                shape=LayerShape(hidden=384, ffn=640, n_experts=16, top_k=3,
+                                                 n_shared=1, gating=SOFTMAX, renormalize=1),
+                                layers=1, prefill_tokens=(40,))}
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("xing4_prefill", 300), ("qwen3next_like", 200),
-                                    ("dsv41_like", 260)])
+                                    ("dsv41_like", 260), ("h384_f640", 40), ("h384_f640", 150)])
 @pytest.mark.parametrize("stage", ["gate_up", "down"])
 def test_grouped_gemm_against_oracle(name, T, stage):
-    wl = WORKLOADS[name]
+    wl = _ODD_K.get(name) or WORKLOADS[name]
     s = wl.shape
     rng = np.random.default_rng(zlib.crc32(f"{name}/{T}/{stage}/gemm".encode()))
     x, ids, w, off, sp, ps = _route_table(wl, T, rng)
