@@ -44,9 +44,9 @@
 // matching up rows (lanes c + 16), so u reaches the lane holding g by one lane swap and SwiGLU
 // is applied in registers.
 //
-// The tile list is built on the device from `offsets` (a prefix of ceil(m_e / 256) over the
-// experts); the grid is an upper bound on the tile count and a workgroup without a tile
-// exits, so nothing depends on host-known expert loads.
+// The tile list is built on the device from `offsets` (whole tiles first, then the experts'
+// last partial tiles by falling height); the grid is an upper bound on the tile count and a
+// workgroup without a tile exits, so nothing depends on host-known expert loads.
 #include <type_traits>
 #include <utility>
 
@@ -425,61 +425,139 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t s_a2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a3[kStageBytes];
   __shared__ int s_pref[1024];
-  __shared__ int s_part[kGemmThreads / 64];
+  __shared__ int s_bin[1024];
+  __shared__ uint64_t s_part[2][kGemmThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // ---- tile prefix over experts: s_pref[e] = sum_{e' <= e} ceil(m_e' / kBM) ----
+  // ---- the tile list, longest first ----
+  // An expert with m slots has m / 256 whole tiles and, if m % 256 > 0, a last tile of
+  // c = ceil((m % 256) / 32) row groups.  The list holds every whole tile (and every last
+  // tile of 8 groups) in expert order, then the last tiles of 7 groups, of 6, .. of 1, each
+  // in expert order: the workgroups are dispatched in list order, so the tiles that take
+  // longest start first and the short ones fill in behind them, instead of a heavy tile
+  // (the shared expert's, the last bin) starting in the last round of workgroups.  Per bin
+  // two packed counters are summed over the bins in one scan: A holds the last tiles of
+  // 1..5 groups (11 bits each), B the whole-tile count (bits 0..20) and the last tiles of 6
+  // and 7 groups (bits 21 and 32).  s_pref[e] = whole tiles of bins 0..e; s_bin[j] = the bin
+  // of the j-th last tile after the whole ones.  Against expert order: 3584/64 gate/up at
+  // 2,048 tokens 285-291 -> 243-247 us, 2048/512 at 2,048 tokens 329-365 -> 310-320 us.  The
+  // down GEMM keeps expert order.
   const int nbins = E + S;
-  int loc[4];
-  int run = 0;
+  int n_whole, total_m;
+  if constexpr (GATEUP) {
+    uint64_t locA[4], locB[4], ownA[4], ownB[4];
+    uint64_t runA = 0, runB = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    int t = 0;
-    if (e < nbins) t = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
-    run += t;
-    loc[i] = run;
-  }
-  int incl = run;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) s_part[wave] = incl;
-  __syncthreads();
-  int before = incl - run;
-  for (int w = 0; w < wave; ++w) before += s_part[w];
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      uint64_t a = 0, b = 0;
+      if (e < nbins) {
+        const int m = offsets[e + 1] - offsets[e];
+        const int c = ((m % kBM) + 31) >> 5;                  // groups of the last tile, 0..8
+        b = (uint64_t)(m / kBM + (c == 8 ? 1 : 0));
+        if (c >= 1 && c <= 5) a = 1ull << (11 * (c - 1));
+        else if (c == 6 || c == 7) b |= 1ull << (21 + 11 * (c - 6));
+      }
+      ownA[i] = a; ownB[i] = b;
+      runA += a; runB += b;
+      locA[i] = runA; locB[i] = runB;
+    }
+    uint64_t inclA = runA, inclB = runB;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t oa = __shfl_up(inclA, d, 64), ob = __shfl_up(inclB, d, 64);
+      if (lane >= d) { inclA += oa; inclB += ob; }
+    }
+    if (lane == 63) { s_part[0][wave] = inclA; s_part[1][wave] = inclB; }
+    __syncthreads();
+    uint64_t beforeA = inclA - runA, beforeB = inclB - runB, totA = 0, totB = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < 1024) s_pref[e] = before + loc[i];
+    for (int w = 0; w < kGemmThreads / 64; ++w) {
+      if (w < wave) { beforeA += s_part[0][w]; beforeB += s_part[1][w]; }
+      totA += s_part[0][w]; totB += s_part[1][w];
+    }
+    auto count_of = [](uint64_t A, uint64_t B, int c) __attribute__((always_inline)) {
+      return (int)(c <= 5 ? (A >> (11 * (c - 1))) & 0x7FF : (B >> (21 + 11 * (c - 6))) & 0x7FF);
+    };
+    const int n_whole_ = (int)(totB & 0x1FFFFF);
+    int start[8];                          // list position of the first last tile of c groups
+    start[7] = n_whole_;
+#pragma unroll
+    for (int c = 6; c >= 1; --c) start[c] = start[c + 1] + count_of(totA, totB, c + 1);
+    const int total_m_ = start[1] + count_of(totA, totB, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e >= nbins) continue;
+      s_pref[e] = (int)((beforeB + locB[i]) & 0x1FFFFF);
+      const uint64_t xa = beforeA + locA[i] - ownA[i], xb = beforeB + locB[i] - ownB[i];
+#pragma unroll
+      for (int c = 1; c <= 7; ++c)
+        if (count_of(ownA[i], ownB[i], c))
+          s_bin[start[c] - n_whole_ + count_of(xa, xb, c)] = e;
+    }
+    __syncthreads();
+
+    n_whole = n_whole_;
+    total_m = total_m_;
+  } else {
+    // expert order, every tile counted as whole: s_pref[e] = sum over e' <= e of
+    // ceil(m_e' / 256) (longest first cost the down GEMM ~3% in this prologue and gained
+    // nothing: its K is short and its output fp32)
+    int loc[4];
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      int t = 0;
+      if (e < nbins) t = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+      run += t;
+      loc[i] = run;
+    }
+    int incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_part[0][wave] = (uint64_t)incl;
+    __syncthreads();
+    int before = incl - run;
+    for (int w = 0; w < wave; ++w) before += (int)s_part[0][w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid * 4 + i;
+      if (e < nbins) s_pref[e] = before + loc[i];
+    }
+    __syncthreads();
+    total_m = n_whole = s_pref[nbins - 1];
   }
-  __syncthreads();
-  const int total_m = s_pref[nbins - 1];
 
   const int K = GATEUP ? H : F;
   const int NT = GATEUP ? F / 128 : (H + kBN - 1) / kBN;
   // XCD-aware order: workgroup b runs on XCD b % 8 (dispatch is round-robin over the XCDs).
-  // XCD x takes M tiles x, x + 8, x + 16, .. and each of them with all its N tiles in a row,
-  // so the workgroups that share an activation panel meet in the same L2, and the heavy M
-  // tiles (the shared expert's and a hot expert's, whole 256-row tiles, next to each other
-  // in the tile list) are spread over the XCDs instead of filling one: against contiguous
-  // ranges of the tile list, 3584/64 at 2,048 tokens gate/up 308 -> 293 us and down 173 ->
-  // 161 us, 7168/384 at 8,192 tokens 569 -> 628 TFLOP/s.  (The list backwards, heavy tiles
-  // first, measured slower.)
+  // XCD x takes M tiles x, x + 8, x + 16, .. of the list and each of them with all its N
+  // tiles in a row, so the workgroups that share an activation panel meet in the same L2,
+  // and the heavy M tiles are spread over the XCDs instead of filling one: against
+  // contiguous ranges of the tile list (in expert order), 3584/64 at 2,048 tokens gate/up
+  // 308 -> 293 us and down 173 -> 161 us, 7168/384 at 8,192 tokens 569 -> 628 TFLOP/s.
   const int xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
   const int mt = xcd + kXcds * (idx / NT), nt = idx % NT;
   if (mt >= total_m) return;
-  // expert owning M tile mt: first e with s_pref[e] > mt
-  int lo = 0, hi = nbins - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (s_pref[mid] > mt) hi = mid; else lo = mid + 1;
+  int e, m0;
+  if (mt < n_whole) {
+    // expert owning whole tile mt: first e with s_pref[e] > mt
+    int lo = 0, hi = nbins - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] > mt) hi = mid; else lo = mid + 1;
+    }
+    e = lo;
+    m0 = (mt - (e ? s_pref[e - 1] : 0)) * kBM;
+  } else {
+    e = s_bin[mt - n_whole];
+    m0 = ((offsets[e + 1] - offsets[e]) / kBM) * kBM;
   }
-  const int e = lo;
-  const int m0 = (mt - (e ? s_pref[e - 1] : 0)) * kBM;
   const int64_t row0 = (int64_t)offsets[e] + m0;
   const int rows_valid = min(kBM, offsets[e + 1] - offsets[e] - m0);
   const int64_t row_bytes = (int64_t)(K >> 5) * kBlockBytes;
