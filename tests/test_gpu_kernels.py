@@ -227,6 +227,34 @@ def test_permute_bitexact(T, k, E):
                               _bf16_rne(x[tok]))
 
 
+@pytest.mark.parametrize("H", [64, 1088, 3584, 8192])
+def test_gather_row_lengths(H):
+    """The slot-row gather at row lengths from a partial workgroup (64) to the 8,192 maximum
+    (eight workgroups a row), fp32 and bf16, bit-exact."""
+    T, k, E = 37, 3, 16
+    rng = np.random.default_rng(H)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    desc = M.make_desc(H, 128, E, k, 1, 0, 1, T)
+    off = torch.empty((E + 2,), dtype=torch.int32, device=DEV)
+    sp = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    ps = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    wsb = M.moe_workspace_size(desc, T)
+    ws = torch.zeros((wsb,), dtype=torch.uint8, device=DEV)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    o_off, o_sp, o_ps = omoe.permute(ids, E, 1)
+    tok = omoe.slot_tokens(o_sp, T, k, 1)
+    xp32 = torch.full((T * (k + 1), H), np.nan, dtype=torch.float32, device=DEV)
+    M.moe_permute(desc, _to_dev(ids), _to_dev(w), T, _to_dev(x), xp32, M.MOE_DTYPE_F32, off, sp, ps,
+                  ws, wsb)
+    xpb = torch.zeros((T * (k + 1), H), dtype=torch.bfloat16, device=DEV)
+    M.moe_permute(desc, _to_dev(ids), _to_dev(w), T, _to_dev(x), xpb, M.MOE_DTYPE_BF16, off, sp, ps,
+                  ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(xp32.cpu().numpy(), x[tok])
+    assert np.array_equal(xpb.cpu().view(torch.int16).numpy().view(np.uint16), _bf16_rne(x[tok]))
+
+
 # ---- expert GEMV (decode) and grouped GEMM (prefill) ---------------------------------
 
 def _route_table(wl, T, rng, force_invalid=False):
