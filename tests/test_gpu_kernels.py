@@ -380,11 +380,18 @@ def test_grouped_gemm_tile_edges(stage):
 _ODD_K = {"h384_f640": Workload(name="h384_f640", cfg_id=13,
                                 shape=LayerShape(hidden=384, ffn=640, n_experts=16, top_k=3,
                                                  n_shared=1, gating=SOFTMAX, renormalize=1),
-                                layers=1, prefill_tokens=(40,))}
+                                layers=1, prefill_tokens=(40,)),
+          # the most bins a layer may have (1,023 experts + the shared one): the tile list's
+          # per-bin scan and last-tile placement at their limit
+          "e1023": Workload(name="e1023", cfg_id=14,
+                            shape=LayerShape(hidden=256, ffn=128, n_experts=1023, top_k=4,
+                                             n_shared=1, gating=SOFTMAX, renormalize=1),
+                            layers=1, prefill_tokens=(600,))}
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("xing4_prefill", 300), ("qwen3next_like", 200),
-                                    ("dsv41_like", 260), ("h384_f640", 40), ("h384_f640", 150)])
+                                    ("dsv41_like", 260), ("h384_f640", 40), ("h384_f640", 150),
+                                    ("e1023", 600)])
 @pytest.mark.parametrize("stage", ["gate_up", "down"])
 def test_grouped_gemm_against_oracle(name, T, stage):
     wl = _ODD_K.get(name) or WORKLOADS[name]
